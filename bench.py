@@ -1,0 +1,195 @@
+"""Benchmark of the block-sparse paged attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2]
+
+A step is one call of the hot path over one batch: for the decode workloads
+msa_sparse_decode (row positions, top-k compaction, paged gather with
+in-register dequant, split attention and merge), for the prefill workload
+msa_sparse_prefill.  Inputs are resident in HBM before timing.  Each step
+reads a different layer's cache (--layers independent copies, rotated), as a
+model's consecutive attention layers do, so no step finds the previous step's
+pages in the 256 MB last-level cache.
+
+Prints one JSON line.  value = algorithmic work of a step / wall time per step
+over the K timed steps; roofline.achieved = the same work / the average kernel
+time of a step from HIP events on the launch stream; cpu_baseline = the fp64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode gathered-KV GB/s (% HBM peak); prefill sparse-attn TFLOP/s (% MFMA)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix, published
+BYTES_PER_TOKEN_HEAD = {"bf16": lambda d: 2 * d * 2, "fp8": lambda d: 2 * d,
+                        "nvfp4": lambda d: 2 * (d // 2 + d // 16)}
+DESCR = {
+    "C1": "tiny decode bf16: 2 requests (seq 1000, 700), dql 1, 4 q / 1 kv heads, head_dim 64, top-k 4",
+    "C2": "decode bf16: batch 64, dql 1, 64 q / 8 kv heads, head_dim 128, top-k 16, seq U[4096, 32768]",
+    "C3": "multi-token decode fp8 e4m3: batch 32, dql 4, 64 q / 8 kv heads, head_dim 128, top-k 32, "
+          "seq U[8192, 65536]",
+    "C4": "ragged causal prefill bf16: 2048/4096/8192/8192 new tokens + 64 padded rows, 64 q / 8 kv heads, "
+          "head_dim 128, top-k 16",
+    "C5": "decode NVFP4: batch 128, dql 1, 64 q / 8 kv heads, head_dim 128, top-k 32, seq U[32768, 131072]",
+}
+
+
+def _cpu_baseline(wl, cache, q, ctx, seconds):
+    """Time the CPU oracle on rows of the workload until `seconds` pass."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    from tests.helpers import compact_oracle_inputs, oracle_positions
+
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    order = rng.permutation(np.flatnonzero(ctx > 0))
+    req, pos = oracle_positions(wl)
+    done, work, elapsed = 0, 0.0, 0.0
+    with threadpool_limits(cores):
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        for start in range(0, len(order), 8):
+            rows = order[start:start + 8]
+            oc, bt, _, _ = compact_oracle_inputs(wl, cache, rows)
+            qf = np.zeros((wl.total_q, wl.num_q_heads, wl.head_dim))
+            qf[rows] = q[rows].float().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.sparse_attention(qf, oc, wl.topk, bt, req, pos, wl.softmax_scale, rows=rows)
+            elapsed += time.perf_counter() - t0
+            done += len(rows)
+            work += float(ctx[rows].sum())
+            if elapsed >= seconds:
+                break
+    if wl.mode == "decode":
+        value = work * wl.num_kv_heads * BYTES_PER_TOKEN_HEAD[wl.kv_dtype](wl.head_dim) / elapsed / 1e9
+        unit = "GB/s"
+    else:
+        value = work * 4 * wl.head_dim * wl.num_q_heads / elapsed / 1e12
+        unit = "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"{done} of {wl.total_q} rows (random, non-empty), {elapsed:.1f} s of fp64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C2", choices=sorted(DESCR))
+    ap.add_argument("--layers", type=int, default=4, help="independent caches rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_paged_query_amd as msa
+    from synth import make_kv_cache, make_query, make_workload
+
+    dev = "cuda"
+    wl = make_workload(args.config)
+    print(f"[bench] {args.config}: building inputs", file=sys.stderr, flush=True)
+    cache = make_kv_cache(wl, dev)
+    q = make_query(wl, dev)
+    topk = torch.from_numpy(wl.topk).to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    seq = torch.from_numpy(wl.seq_lens).to(dev)
+    cu = None if wl.cu_seqlens_q is None else torch.from_numpy(wl.cu_seqlens_q).to(dev)
+    ks = vs = None
+    if wl.kv_dtype != "bf16":
+        ks = torch.tensor([cache["k_scale"]], dtype=torch.float32, device=dev)
+        vs = torch.tensor([cache["v_scale"]], dtype=torch.float32, device=dev)
+    layers = []
+    for i in range(max(args.layers, 1)):
+        kp = cache["k_pages"] if i == 0 else cache["k_pages"].clone()
+        vp = cache["v_pages"]
+        if vp is not None and i > 0:
+            vp = vp.clone()
+        layers.append(msa.KVCache(wl.kv_dtype, kp, vp, wl.num_kv_heads, wl.head_dim, wl.block_page_stride, ks, vs))
+    out = torch.empty_like(q)
+
+    # work of one step, from the library's own context lengths
+    if wl.mode == "decode":
+        _, ctx = msa.msa_build_sparse_block_table(topk, bt, seq_lens=seq, decode_query_len=wl.decode_query_len)
+    else:
+        qlen = np.diff(wl.cu_seqlens_q)
+        req_id, abs_pos = msa.msa_query_token_positions(cu, seq - torch.from_numpy(qlen).to(dev, torch.int32),
+                                                         wl.total_q)
+        _, ctx = msa.msa_build_sparse_block_table(topk, bt, query_req_id=req_id, query_abs_pos=abs_pos)
+    ctx = ctx.cpu().numpy().astype(np.int64)
+    sum_ctx = int(ctx.sum())
+    if wl.mode == "decode":
+        work = sum_ctx * wl.num_kv_heads * BYTES_PER_TOKEN_HEAD[wl.kv_dtype](wl.head_dim)   # bytes
+        ws = torch.empty(max(msa.msa_decode_workspace_size(wl.total_q, wl.num_q_heads, wl.head_dim, wl.topk_k), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def step(i):
+            msa.msa_sparse_decode(q, layers[i % len(layers)], topk, bt, seq, wl.softmax_scale,
+                                  decode_query_len=wl.decode_query_len, out=out, workspace=ws)
+    else:
+        work = 4.0 * wl.head_dim * wl.num_q_heads * sum_ctx                                   # flops
+
+        def step(i):
+            msa.msa_sparse_prefill(q, layers[i % len(layers)], topk, bt, cu, seq, wl.softmax_scale, out=out)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    ms_per_step = wall * 1e3 / args.steps
+    if wl.mode == "decode":
+        value, unit = work / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        achieved = work / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+        dtype = "f16" if wl.kv_dtype == "nvfp4" else "bf16"
+    else:
+        value, unit = work / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+        achieved = work / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        dtype = "bf16"
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = _cpu_baseline(wl, cache, q, ctx, args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": f"{args.config} {DESCR[args.config]}", "rows": wl.total_q,
+                   "sum_ctx": sum_ctx, "kernel_ms": kernel_ms, "layers": len(layers)},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

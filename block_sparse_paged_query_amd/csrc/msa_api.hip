@@ -1,0 +1,350 @@
+// C ABI of libmsa: argument validation (before any HIP call), workspace and
+// split selection, and launches on the caller's stream.  Declarations and the
+// contract of every entry point are in include/msa.h.
+#include <stdio.h>
+#include <stdarg.h>
+#include <string.h>
+
+#include "../../include/msa.h"
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+msa_status_t fail(msa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+msa_status_t ok() {
+  g_last_error[0] = 0;
+  return MSA_OK;
+}
+
+msa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MSA_CHECK(cond, st, ...) \
+  do {                           \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+int fmt_of(int32_t kv_dtype) {
+  switch (kv_dtype) {
+    case MSA_BF16: return msa::kFmtBf16;
+    case MSA_FP8_E4M3FN: return msa::kFmtFp8;
+    case MSA_NVFP4: return msa::kFmtNvfp4;
+    default: return -1;
+  }
+}
+
+// Validation shared by the attends.
+msa_status_t check_attend(const void* q, int32_t q_dtype, int32_t rows, int32_t num_q_heads, const msa_kv_cache_t* kv,
+                          const int32_t* topk, int64_t topk_row_stride, int32_t topk_k, const int32_t* block_table,
+                          int64_t bt_row_stride, int32_t bt_cols, const void* out, float softmax_scale) {
+  MSA_CHECK(kv != nullptr, MSA_ERR_INVALID_ARGUMENT, "kv cache descriptor is NULL");
+  MSA_CHECK(rows >= 0, MSA_ERR_INVALID_ARGUMENT, "row count %d is negative", rows);
+  MSA_CHECK(q_dtype == MSA_BF16, MSA_ERR_UNSUPPORTED, "q dtype %d: only bf16 queries are served", q_dtype);
+  MSA_CHECK(fmt_of(kv->kv_dtype) >= 0, MSA_ERR_UNSUPPORTED, "kv dtype %d: bf16, fp8 e4m3fn or nvfp4 pages only",
+            kv->kv_dtype);
+  MSA_CHECK(kv->head_dim == 64 || kv->head_dim == 128, MSA_ERR_UNSUPPORTED, "head_dim %d: 64 or 128 only",
+            kv->head_dim);
+  MSA_CHECK(kv->kv_dtype != MSA_NVFP4 || kv->head_dim == 128, MSA_ERR_UNSUPPORTED,
+            "nvfp4 pages need head_dim 128 (got %d)", kv->head_dim);
+  MSA_CHECK(kv->num_kv_heads >= 1, MSA_ERR_INVALID_ARGUMENT, "num_kv_heads %d < 1", kv->num_kv_heads);
+  MSA_CHECK(num_q_heads >= 1 && num_q_heads % kv->num_kv_heads == 0, MSA_ERR_INVALID_ARGUMENT,
+            "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, kv->num_kv_heads);
+  MSA_CHECK(num_q_heads / kv->num_kv_heads <= 16, MSA_ERR_UNSUPPORTED,
+            "%d query heads per kv head: at most 16 are served", num_q_heads / kv->num_kv_heads);
+  MSA_CHECK(kv->block_page_stride == 8 || kv->block_page_stride == 16, MSA_ERR_INVALID_ARGUMENT,
+            "block_page_stride %d: 8 (separate K/V planes) or 16 (both sides in a block)", kv->block_page_stride);
+  MSA_CHECK(topk_k >= 1 && topk_k <= msa::kMaxTopK, MSA_ERR_UNSUPPORTED, "topk_k %d: 1..%d", topk_k, msa::kMaxTopK);
+  MSA_CHECK(topk_row_stride >= topk_k, MSA_ERR_INVALID_ARGUMENT, "topk row stride %lld < topk_k %d",
+            (long long)topk_row_stride, topk_k);
+  MSA_CHECK(bt_cols >= 0 && bt_row_stride >= bt_cols, MSA_ERR_INVALID_ARGUMENT,
+            "block_table: %d columns, row stride %lld", bt_cols, (long long)bt_row_stride);
+  MSA_CHECK(kv->num_pages >= 0, MSA_ERR_INVALID_ARGUMENT, "num_pages %lld < 0", (long long)kv->num_pages);
+  const int esz = kv->kv_dtype == MSA_BF16 ? 2 : 1;
+  const int64_t page_min = kv->kv_dtype == MSA_NVFP4 ? (int64_t)2 * kv->num_kv_heads * 9 * kv->head_dim
+                                                      : (int64_t)kv->num_kv_heads * 16 * kv->head_dim * esz;
+  MSA_CHECK(kv->page_stride_bytes >= page_min && kv->page_stride_bytes % 16 == 0, MSA_ERR_INVALID_ARGUMENT,
+            "page stride %lld bytes: need a multiple of 16 and >= %lld", (long long)kv->page_stride_bytes,
+            (long long)page_min);
+  MSA_CHECK(softmax_scale == softmax_scale, MSA_ERR_INVALID_ARGUMENT, "softmax_scale is NaN");
+  if (rows > 0) {
+    MSA_CHECK(q && out && topk && block_table && kv->k_pages, MSA_ERR_INVALID_ARGUMENT,
+              "q, out, topk, block_table and k_pages must be non-NULL");
+    MSA_CHECK(kv->kv_dtype == MSA_NVFP4 || kv->v_pages, MSA_ERR_INVALID_ARGUMENT, "v_pages is NULL");
+    MSA_CHECK(((uintptr_t)q % 16) == 0 && ((uintptr_t)out % 16) == 0 && ((uintptr_t)kv->k_pages % 16) == 0 &&
+                  (kv->kv_dtype == MSA_NVFP4 || ((uintptr_t)kv->v_pages % 16) == 0),
+              MSA_ERR_INVALID_ARGUMENT, "q, out and page buffers must be 16-byte aligned");
+  }
+  return MSA_OK;
+}
+
+msa::AttendArgs attend_args(const void* q, int32_t num_q_heads, const msa_kv_cache_t* kv, const int32_t* topk,
+                            int64_t topk_row_stride, int32_t topk_k, const int32_t* block_table, int64_t bt_row_stride,
+                            int32_t bt_cols, float softmax_scale, void* out) {
+  msa::AttendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.out = out;
+  a.topk = topk;
+  a.topk_stride = topk_row_stride;
+  a.topk_k = topk_k;
+  a.block_table = block_table;
+  a.bt_stride = bt_row_stride;
+  a.bt_cols = bt_cols;
+  a.k_base = static_cast<const uint8_t*>(kv->k_pages);
+  a.v_base = static_cast<const uint8_t*>(kv->kv_dtype == MSA_NVFP4 ? kv->k_pages : kv->v_pages);
+  a.page_stride = kv->page_stride_bytes;
+  a.num_pages = kv->num_pages;
+  a.block_page_stride = kv->block_page_stride;
+  a.v_page_offset = kv->kv_dtype == MSA_NVFP4 ? 0 : kv->block_page_stride - msa::kPagesPerBlock;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
+  a.softmax_scale = softmax_scale;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = kv->num_kv_heads;
+  a.group = num_q_heads / kv->num_kv_heads;
+  a.head_dim = kv->head_dim;
+  a.nsplit = 1;
+  return a;
+}
+
+size_t split_bytes(int64_t rows, int32_t num_q_heads, int32_t head_dim, int32_t nsplit) {
+  return (size_t)(rows * num_q_heads * nsplit) * (size_t)(head_dim + 2) * sizeof(float) + 256;
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// Splits per (row, kv head): enough workgroups for two per compute unit, each
+// split keeping at least one 128-token block per wave.
+int choose_splits(int64_t rows, int32_t num_kv_heads, int32_t topk_k, int cus) {
+  const int64_t units = rows * num_kv_heads;
+  if (units <= 0) return 1;
+  int64_t ns = (2 * (int64_t)cus + units - 1) / units;
+  const int64_t max_ns = topk_k > 1 ? topk_k : 1;   // 4 chunks per block, 4 waves per split
+  if (ns > max_ns) ns = max_ns;
+  if (ns > 64) ns = 64;
+  return ns < 1 ? 1 : (int)ns;
+}
+
+}  // namespace
+
+extern "C" {
+
+MSA_API const char* msa_last_error(void) { return g_last_error; }
+
+MSA_API msa_status_t msa_build_sparse_block_table(const int32_t* topk, int64_t topk_row_stride, int32_t topk_k,
+                                                  int32_t total_q, const int32_t* block_table, int64_t bt_row_stride,
+                                                  int32_t bt_cols, int32_t num_reqs, const int32_t* seq_lens,
+                                                  int32_t decode_query_len, const int32_t* query_req_id,
+                                                  const int32_t* query_abs_pos, int32_t block_page_stride,
+                                                  int32_t* sparse_bt, int64_t sbt_row_stride, int32_t* sparse_ctx,
+                                                  hipStream_t stream) {
+  MSA_CHECK(total_q >= 0 && num_reqs >= 0, MSA_ERR_INVALID_ARGUMENT, "negative total_q %d or num_reqs %d", total_q,
+            num_reqs);
+  MSA_CHECK(topk_k >= 1 && topk_k <= msa::kMaxTopK, MSA_ERR_UNSUPPORTED, "topk_k %d: 1..%d", topk_k, msa::kMaxTopK);
+  MSA_CHECK(topk_row_stride >= topk_k, MSA_ERR_INVALID_ARGUMENT, "topk row stride %lld < topk_k %d",
+            (long long)topk_row_stride, topk_k);
+  MSA_CHECK(bt_cols >= 0 && bt_row_stride >= bt_cols, MSA_ERR_INVALID_ARGUMENT,
+            "block_table: %d columns, row stride %lld", bt_cols, (long long)bt_row_stride);
+  MSA_CHECK(block_page_stride >= 1, MSA_ERR_INVALID_ARGUMENT, "block_page_stride %d < 1", block_page_stride);
+  MSA_CHECK(sbt_row_stride >= (int64_t)topk_k * msa::kPagesPerBlock, MSA_ERR_INVALID_ARGUMENT,
+            "sparse_bt row stride %lld < 8 * topk_k", (long long)sbt_row_stride);
+  MSA_CHECK((query_req_id == nullptr) == (query_abs_pos == nullptr), MSA_ERR_INVALID_ARGUMENT,
+            "prefill mode needs both query_req_id and query_abs_pos");
+  if (query_req_id == nullptr) {
+    MSA_CHECK(decode_query_len >= 1, MSA_ERR_INVALID_ARGUMENT, "decode_query_len %d < 1", decode_query_len);
+    MSA_CHECK((int64_t)total_q == (int64_t)num_reqs * decode_query_len, MSA_ERR_INVALID_ARGUMENT,
+              "decode top-k rows must equal batch * decode_query_len: %d != %d * %d", total_q, num_reqs,
+              decode_query_len);
+  }
+  if (total_q == 0) return ok();
+  MSA_CHECK(topk && sparse_bt && sparse_ctx && (block_table || bt_cols == 0), MSA_ERR_INVALID_ARGUMENT,
+            "topk, block_table, sparse_bt and sparse_ctx must be non-NULL");
+  MSA_CHECK(query_req_id != nullptr || seq_lens != nullptr, MSA_ERR_INVALID_ARGUMENT, "decode mode needs seq_lens");
+  MSA_CHECK(num_reqs >= 1, MSA_ERR_INVALID_ARGUMENT, "rows without requests");
+  msa::TableArgs a;
+  a.topk = topk;
+  a.topk_stride = topk_row_stride;
+  a.topk_k = topk_k;
+  a.total_q = total_q;
+  a.block_table = block_table;
+  a.bt_stride = bt_row_stride;
+  a.bt_cols = bt_cols;
+  a.num_reqs = num_reqs;
+  a.seq_lens = seq_lens;
+  a.dql = decode_query_len;
+  a.query_req_id = query_req_id;
+  a.query_abs_pos = query_abs_pos;
+  a.block_page_stride = block_page_stride;
+  a.sparse_bt = sparse_bt;
+  a.sbt_stride = sbt_row_stride;
+  a.sparse_ctx = sparse_ctx;
+  return hip_status(msa::launch_sparse_table(a, stream), "sparse table launch");
+}
+
+MSA_API msa_status_t msa_query_token_positions(const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                               int32_t num_reqs, int32_t total_q, int32_t* query_req_id,
+                                               int32_t* query_abs_pos, hipStream_t stream) {
+  MSA_CHECK(num_reqs >= 0 && total_q >= 0, MSA_ERR_INVALID_ARGUMENT, "negative num_reqs %d or total_q %d", num_reqs,
+            total_q);
+  if (total_q == 0) return ok();
+  MSA_CHECK(cu_seqlens_q && query_req_id && query_abs_pos && (context_lens || num_reqs == 0),
+            MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  return hip_status(msa::launch_query_positions(cu_seqlens_q, context_lens, num_reqs, total_q, query_req_id,
+                                                query_abs_pos, stream),
+                    "query positions launch");
+}
+
+MSA_API size_t msa_decode_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim, int32_t topk_k) {
+  if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const int max_ns = topk_k > 64 ? 64 : (topk_k < 1 ? 1 : topk_k);
+  return split_bytes(total_q, num_q_heads, head_dim, max_ns);
+}
+
+MSA_API msa_status_t msa_sparse_decode(const void* q, int32_t q_dtype, int32_t num_reqs, int32_t decode_query_len,
+                                       int32_t num_q_heads, const msa_kv_cache_t* kv, const int32_t* topk,
+                                       int64_t topk_row_stride, int32_t topk_k, const int32_t* block_table,
+                                       int64_t bt_row_stride, int32_t bt_cols, const int32_t* seq_lens,
+                                       float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  MSA_CHECK(num_reqs >= 0 && decode_query_len >= 1, MSA_ERR_INVALID_ARGUMENT, "num_reqs %d, decode_query_len %d",
+            num_reqs, decode_query_len);
+  const int64_t rows64 = (int64_t)num_reqs * decode_query_len;
+  MSA_CHECK(rows64 <= (1 << 24), MSA_ERR_UNSUPPORTED, "%lld decode rows: at most 2^24", (long long)rows64);
+  const int32_t rows = (int32_t)rows64;
+  msa_status_t st = check_attend(q, q_dtype, rows, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table,
+                                 bt_row_stride, bt_cols, out, softmax_scale);
+  if (st != MSA_OK) return st;
+  if (rows == 0) return ok();
+  MSA_CHECK(seq_lens != nullptr, MSA_ERR_INVALID_ARGUMENT, "seq_lens is NULL");
+  msa::AttendArgs a = attend_args(q, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table, bt_row_stride,
+                                  bt_cols, softmax_scale, out);
+  a.seq_lens = seq_lens;
+  a.dql = decode_query_len;
+  a.num_reqs = num_reqs;
+  int ns = choose_splits(rows, kv->num_kv_heads, topk_k, device_cus());
+  while (ns > 1 && (workspace == nullptr || split_bytes(rows, num_q_heads, kv->head_dim, ns) > workspace_bytes)) --ns;
+  a.nsplit = ns;
+  if (ns > 1) {
+    const uintptr_t base = ((uintptr_t)workspace + 255) & ~(uintptr_t)255;
+    a.ws_o = reinterpret_cast<float*>(base);
+    a.ws_ml = a.ws_o + (size_t)rows * num_q_heads * ns * kv->head_dim;
+  }
+  return hip_status(msa::launch_attend_rows(a, fmt_of(kv->kv_dtype), msa::kModeDecode, rows, stream),
+                    "decode launch");
+}
+
+MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim, int32_t topk_k) {
+  (void)total_q;
+  (void)num_q_heads;
+  (void)head_dim;
+  (void)topk_k;
+  return 0;
+}
+
+MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,
+                                        const msa_kv_cache_t* kv, const int32_t* topk, int64_t topk_row_stride,
+                                        int32_t topk_k, const int32_t* block_table, int64_t bt_row_stride,
+                                        int32_t bt_cols, int32_t num_reqs, const int32_t* cu_seqlens_q,
+                                        const int32_t* seq_lens, float softmax_scale, void* out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  MSA_CHECK(total_q >= 0 && num_reqs >= 0, MSA_ERR_INVALID_ARGUMENT, "negative total_q %d or num_reqs %d", total_q,
+            num_reqs);
+  MSA_CHECK(total_q <= (1 << 24), MSA_ERR_UNSUPPORTED, "%d prefill rows: at most 2^24", total_q);
+  msa_status_t st = check_attend(q, q_dtype, total_q, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table,
+                                 bt_row_stride, bt_cols, out, softmax_scale);
+  if (st != MSA_OK) return st;
+  MSA_CHECK(kv->kv_dtype == MSA_BF16, MSA_ERR_UNSUPPORTED, "prefill serves bf16 pages only (got dtype %d)",
+            kv->kv_dtype);
+  if (total_q == 0) return ok();
+  MSA_CHECK(num_reqs >= 1 && cu_seqlens_q && seq_lens, MSA_ERR_INVALID_ARGUMENT,
+            "prefill needs num_reqs >= 1, cu_seqlens_q and seq_lens");
+  msa::AttendArgs a = attend_args(q, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table, bt_row_stride,
+                                  bt_cols, softmax_scale, out);
+  a.seq_lens = seq_lens;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.num_reqs = num_reqs;
+  a.dql = 1;
+  return hip_status(msa::launch_attend_rows(a, fmt_of(kv->kv_dtype), msa::kModePrefill, total_q, stream),
+                    "prefill launch");
+}
+
+MSA_API msa_status_t msa_insert_index_cache(const void* index_k, int64_t k_stride0, int64_t k_stride1, int32_t n,
+                                            int32_t d, int32_t dtype, void* index_cache, int64_t c_stride0,
+                                            int64_t c_stride1, int64_t c_stride2, int32_t num_blocks,
+                                            int32_t cache_block_size, const int64_t* slot_mapping,
+                                            int64_t slot_stride, hipStream_t stream) {
+  MSA_CHECK(n >= 0 && d >= 0 && num_blocks >= 0 && cache_block_size >= 0, MSA_ERR_INVALID_ARGUMENT,
+            "negative size (n %d, d %d, blocks %d, block size %d)", n, d, num_blocks, cache_block_size);
+  if (n == 0 || d == 0 || num_blocks == 0 || cache_block_size == 0) return ok();
+  MSA_CHECK(c_stride2 == 1, MSA_ERR_INVALID_ARGUMENT, "index cache requires contiguous head dimension");
+  int esize = 0;
+  switch (dtype) {
+    case MSA_BF16:
+    case MSA_FP16: esize = 2; break;
+    case MSA_FP32: esize = 4; break;
+    case MSA_FP8_E4M3FN: esize = 1; break;
+    default: return fail(MSA_ERR_UNSUPPORTED, "index key dtype %d: bf16, fp16, fp32 or fp8 only", dtype);
+  }
+  MSA_CHECK(index_k && index_cache && slot_mapping, MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  return hip_status(msa::launch_index_insert(index_k, k_stride0, k_stride1, n, d, esize, index_cache, c_stride0,
+                                             c_stride1, num_blocks, cache_block_size, slot_mapping, slot_stride,
+                                             stream),
+                    "index cache launch");
+}
+
+MSA_API msa_status_t msa_debug_dequant_tokens(const msa_kv_cache_t* kv, const int32_t* pages, const int32_t* slots,
+                                              int32_t n, float* k_out, float* v_out, hipStream_t stream) {
+  MSA_CHECK(kv != nullptr && n >= 0, MSA_ERR_INVALID_ARGUMENT, "NULL kv or negative n");
+  MSA_CHECK(fmt_of(kv->kv_dtype) >= 0, MSA_ERR_UNSUPPORTED, "kv dtype %d", kv->kv_dtype);
+  MSA_CHECK(kv->head_dim >= 16 && kv->head_dim % 16 == 0 && kv->num_kv_heads >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "head_dim %d / num_kv_heads %d", kv->head_dim, kv->num_kv_heads);
+  MSA_CHECK(kv->block_page_stride == 8 || kv->block_page_stride == 16, MSA_ERR_INVALID_ARGUMENT,
+            "block_page_stride %d", kv->block_page_stride);
+  if (n == 0) return ok();
+  MSA_CHECK(pages && slots && k_out && v_out && kv->k_pages && (kv->kv_dtype == MSA_NVFP4 || kv->v_pages),
+            MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  msa::DequantArgs a;
+  a.fmt = fmt_of(kv->kv_dtype);
+  a.num_kv_heads = kv->num_kv_heads;
+  a.head_dim = kv->head_dim;
+  a.v_page_offset = kv->kv_dtype == MSA_NVFP4 ? 0 : kv->block_page_stride - msa::kPagesPerBlock;
+  a.k_base = static_cast<const uint8_t*>(kv->k_pages);
+  a.v_base = static_cast<const uint8_t*>(kv->kv_dtype == MSA_NVFP4 ? kv->k_pages : kv->v_pages);
+  a.page_stride = kv->page_stride_bytes;
+  a.num_pages = kv->num_pages;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
+  a.pages = pages;
+  a.slots = slots;
+  a.n = n;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  return hip_status(msa::launch_debug_dequant(a, stream), "dequant hook launch");
+}
+
+}  // extern "C"

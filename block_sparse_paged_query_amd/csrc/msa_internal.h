@@ -1,0 +1,93 @@
+// Internal launch interfaces between the C ABI (msa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+enum RowMode : int { kModeDecode = 0, kModePrefill = 1 };
+
+// Arguments of the row-wise attend (decode rows, or prefill rows one by one).
+struct AttendArgs {
+  const void* q;
+  void* out;
+  const int32_t* topk;
+  int64_t topk_stride;
+  int32_t topk_k;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int32_t bt_cols;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  int32_t dql;
+  int32_t num_reqs;
+  const uint8_t* k_base;
+  const uint8_t* v_base;
+  int64_t page_stride;
+  int64_t num_pages;
+  int32_t block_page_stride;
+  int32_t v_page_offset;
+  const float* k_scale;
+  const float* v_scale;
+  float softmax_scale;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t head_dim;
+  int32_t nsplit;
+  float* ws_o;    // [rows][Hq][nsplit][D]
+  float* ws_ml;   // [rows][Hq][nsplit][2]
+};
+
+hipError_t launch_attend_rows(const AttendArgs& a, int fmt, int mode, int rows, hipStream_t stream);
+
+struct TableArgs {
+  const int32_t* topk;
+  int64_t topk_stride;
+  int32_t topk_k;
+  int32_t total_q;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int32_t bt_cols;
+  int32_t num_reqs;
+  const int32_t* seq_lens;
+  int32_t dql;
+  const int32_t* query_req_id;
+  const int32_t* query_abs_pos;
+  int32_t block_page_stride;
+  int32_t* sparse_bt;
+  int64_t sbt_stride;
+  int32_t* sparse_ctx;
+};
+
+hipError_t launch_sparse_table(const TableArgs& a, hipStream_t stream);
+
+hipError_t launch_query_positions(const int32_t* cu, const int32_t* context_lens, int num_reqs, int total_q,
+                                  int32_t* req_id, int32_t* abs_pos, hipStream_t stream);
+
+hipError_t launch_index_insert(const void* k, int64_t ks0, int64_t ks1, int n, int d, int esize, void* cache,
+                               int64_t cs0, int64_t cs1, int num_blocks, int block_size, const int64_t* slots,
+                               int64_t slot_stride, hipStream_t stream);
+
+struct DequantArgs {
+  int fmt;
+  int num_kv_heads;
+  int head_dim;
+  int v_page_offset;
+  const uint8_t* k_base;
+  const uint8_t* v_base;
+  int64_t page_stride;
+  int64_t num_pages;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* pages;
+  const int32_t* slots;
+  int n;
+  float* k_out;
+  float* v_out;
+};
+
+hipError_t launch_debug_dequant(const DequantArgs& a, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,251 @@
+/*
+ * msa.h -- C ABI of libmsa: MiniMax-M3 block-sparse attention over a paged
+ * KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is described on three vLLM API documentation pages, cited here
+ * by title and section:
+ *   [FI]  vllm.models.minimax_m3.nvidia.sparse_attention_flashinfer
+ *   [NV4] vllm.models.minimax_m3.amd.sparse_attention_nvfp4
+ *   [SPA] vllm.models.minimax_m3.amd.ops.sparse_pa
+ *
+ * Each query token attends only to the 128-token KV blocks named in its
+ * top-k row, clipped causally: ids past the token's own block are dropped and
+ * the own block is attended up to the token's position ([SPA]
+ * _write_sparse_block_table_row_from_values).
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *    stated otherwise.  The library never allocates, frees or synchronises;
+ *    work is enqueued on `stream` (0 = the null stream).
+ *  - All host-visible arguments are validated before any HIP call; on error
+ *    nothing is launched and msa_last_error() describes the problem.
+ *    Values held in device memory (ids, lengths) are not read on the host.
+ *  - Empty work (no rows / no keys) returns MSA_OK and launches nothing,
+ *    as [SPA] minimax_m3_insert_index_cache does on empty input.
+ *  - A sparse block is 128 tokens; pages hold 16 tokens; a block spans
+ *    `block_page_stride` page ids (8 when K and V are separate planes, 16
+ *    when one buffer holds both sides of a block), [SPA]
+ *    minimax_m3_sparse_block_page_stride.  Physical page ids and byte
+ *    offsets are 64-bit, [NV4] supported_kv_cache_layouts.
+ *  - Rows of a top-k table must hold distinct non-negative ids (-1 pads).
+ *    Repeated ids are outside the contract (the printed routine counts them
+ *    twice); the library stays in bounds but the result is unspecified.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_API __attribute__((visibility("default")))
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = 1,   /* a value a caller must fix ([SPA] ValueError / assertion) */
+  MSA_ERR_UNSUPPORTED = 2,        /* a valid shape / dtype this build does not serve */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MSA_ERR_HIP = 4                 /* a HIP launch failed; see msa_last_error() */
+} msa_status_t;
+
+typedef enum msa_dtype {
+  MSA_BF16 = 0,
+  MSA_FP16 = 1,
+  MSA_FP8_E4M3FN = 2,   /* OCP E4M3FN: max 448, NaN = S.1111.111 */
+  MSA_NVFP4 = 3,        /* e2m1 codes + one E4M3FN scale per 16 elements */
+  MSA_FP32 = 4
+} msa_dtype_t;
+
+/*
+ * One layer's paged K/V cache.  [FI] MiniMaxM3SparseFlashInferImpl.forward
+ * (K and V views of the cache, fp8 view with per-tensor scales);
+ * [NV4] customize_spec (NVFP4: two head slots per kv head, packed data plus
+ * block scales, bytes laid out for the kernel).
+ *
+ * kv_dtype MSA_BF16 / MSA_FP8_E4M3FN: K and V are planes of pages
+ *   [page][num_kv_heads][16 tokens][head_dim] elements, page p at byte
+ *   p * page_stride_bytes of its buffer.  With block_page_stride 8, block b
+ *   owns pages 8b..8b+7 of k_pages (K) and of v_pages (V).  With stride 16,
+ *   block b owns pages 16b..16b+15: K in 16b..16b+7 of k_pages, V in
+ *   16b+8..16b+15 of v_pages (usually the same buffer).
+ * kv_dtype MSA_NVFP4 (head_dim 128): one buffer k_pages of pages
+ *   [page][2 * num_kv_heads slots][9 * head_dim bytes]; slot 2g is K and
+ *   slot 2g+1 is V of kv head g; v_pages is ignored.  Inside a slot, bytes
+ *   [0, 8*head_dim) hold token t's e2m1 codes at t*head_dim/2 + d/2 (low
+ *   nibble = even d); bytes [8*head_dim, 9*head_dim) hold token t's E4M3FN
+ *   scale of elements 16u..16u+15 at 8*head_dim + t*head_dim/16 + u.
+ *
+ * k_scale / v_scale: device fp32 scalars (NULL = 1.0).  fp8: the
+ *   per-tensor dequant multipliers; NVFP4: the per-tensor global scales.
+ *   They fold exactly into the softmax scale and the output scale
+ *   ([FI] forward: logits are linear in K, the output in V).
+ * num_pages: pages each buffer holds.  Blocks whose pages fall outside
+ *   [0, num_pages) are skipped (they add nothing), so a bad table cannot
+ *   make the attend read out of bounds.
+ */
+typedef struct msa_kv_cache {
+  int32_t kv_dtype;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_page_stride;
+  const void* k_pages;
+  const void* v_pages;
+  int64_t page_stride_bytes;
+  int64_t num_pages;
+  const float* k_scale;
+  const float* v_scale;
+} msa_kv_cache_t;
+
+/* Thread-local description of the last error returned on this thread. */
+MSA_API const char* msa_last_error(void);
+
+/*
+ * Page-16 sparse block table, one row per query token.
+ * [SPA] _write_sparse_block_table_row_from_values,
+ * minimax_m3_build_sparse_block_table_decode / _prefill.
+ *
+ * topk [total_q][topk_k] int32 (row stride topk_row_stride elements):
+ *   logical 128-token block ids, -1 padded, one index head shared by all
+ *   attention heads.
+ * block_table [num_reqs][bt_cols] int32 (row stride bt_row_stride): a
+ *   request's logical block -> physical block id.
+ * Row positions, one of two modes:
+ *   decode  (query_req_id == NULL): total_q must equal num_reqs *
+ *     decode_query_len (the [SPA] decode builder's assertion); row i belongs
+ *     to request i / dql at position seq_lens[r] - dql + i % dql
+ *     (right-aligned, [FI] forward);
+ *   prefill (query_req_id and query_abs_pos non-NULL, [total_q] int32 each):
+ *     rows with a negative position or a request id outside [0, num_reqs)
+ *     are padding.
+ * Per row: causal length = max(pos + 1, 0), own block = pos / 128; an id is
+ * kept if 0 <= id <= own block and id < bt_cols.  Kept earlier ("full")
+ * blocks fill the slots first, in row order, then the own ("tail") block.
+ * Slot s holds block_table[r][id] * block_page_stride + j at 8s + j
+ * (j < 8); the rest of the row, up to 8 * topk_k, is zero.
+ * sparse_ctx[i] = 128 * full + tail tokens (pos + 1 - 128 * own) when the
+ * own block is kept, else min(128 * kept, causal length).
+ * Outputs: sparse_bt [total_q][8 * topk_k] int32 (row stride
+ * sbt_row_stride >= 8 * topk_k), sparse_ctx [total_q] int32.
+ */
+MSA_API msa_status_t msa_build_sparse_block_table(
+    const int32_t* topk, int64_t topk_row_stride, int32_t topk_k, int32_t total_q,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t bt_cols, int32_t num_reqs,
+    const int32_t* seq_lens, int32_t decode_query_len,
+    const int32_t* query_req_id, const int32_t* query_abs_pos,
+    int32_t block_page_stride,
+    int32_t* sparse_bt, int64_t sbt_row_stride, int32_t* sparse_ctx,
+    hipStream_t stream);
+
+/*
+ * Request id and absolute position of each prefill token.
+ * [NV4] MiniMaxM3SparseRocmNvfp4MetadataBuilder.build
+ * (minimax_m3_query_token_positions; its body is not printed).
+ * Token t of request r (cu_seqlens_q[r] <= t < cu_seqlens_q[r+1]) sits at
+ * context_lens[r] + t - cu_seqlens_q[r]; tokens t >= cu_seqlens_q[num_reqs]
+ * (up to total_q) are padding: request 0, position -1.
+ * cu_seqlens_q [num_reqs + 1], context_lens [num_reqs] int32 in;
+ * query_req_id, query_abs_pos [total_q] int32 out.
+ */
+MSA_API msa_status_t msa_query_token_positions(
+    const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_reqs, int32_t total_q,
+    int32_t* query_req_id, int32_t* query_abs_pos, hipStream_t stream);
+
+/*
+ * Bytes of workspace msa_sparse_decode can use for split-K partials.
+ * Passing fewer (or NULL) is allowed: the call then uses fewer splits.
+ */
+MSA_API size_t msa_decode_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t topk_k);
+
+/*
+ * Block-sparse GQA decode, decode_query_len >= 1 tokens per request.
+ * [FI] MiniMaxM3SparseFlashInferImpl.forward (msa_sparse_decode_attention:
+ * q, K/V cache, top-k, page table, seqused_k, seqlen_q, causal, softmax
+ * scale, v scale, out); [NV4] MiniMaxM3SparseRocmNvfp4Impl.forward
+ * (the NVFP4 decode with k_scale / v_scale and decode_query_len).
+ *
+ * q, out [num_reqs * decode_query_len][num_q_heads][head_dim] bf16,
+ * contiguous (q_dtype must be MSA_BF16).  Query head h reads kv head
+ * h / (num_q_heads / num_kv_heads).  Row positions, top-k clipping and
+ * table lookup as in msa_build_sparse_block_table (decode mode).
+ * out = softmax(softmax_scale * k_scale * q K^T over the row's tokens) V
+ *       * v_scale, with K, V the stored codes; a row with no tokens gets 0.
+ * Compute: bf16 (fp16 for NVFP4, where e2m1 x E4M3 products are exact)
+ * matrix-core inputs, fp32 accumulation and softmax, output rounded to
+ * nearest even.
+ * topk_k <= 1024; head_dim 64 or 128 (NVFP4: 128);
+ * num_q_heads / num_kv_heads <= 16.
+ */
+MSA_API msa_status_t msa_sparse_decode(
+    const void* q, int32_t q_dtype, int32_t num_reqs, int32_t decode_query_len, int32_t num_q_heads,
+    const msa_kv_cache_t* kv,
+    const int32_t* topk, int64_t topk_row_stride, int32_t topk_k,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t bt_cols,
+    const int32_t* seq_lens,
+    float softmax_scale, void* out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace msa_sparse_prefill needs (0 today; reserved). */
+MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                          int32_t topk_k);
+
+/*
+ * Block-sparse ragged causal prefill.
+ * [FI] MiniMaxM3SparseFlashInferImpl.forward (msa_sparse_attention:
+ * q, K/V cache, top-k, cu_seqlens_q, causal, softmax scale, page table,
+ * seqused_k, v scale, out); [NV4] MiniMaxM3SparseRocmNvfp4Impl.forward
+ * (the prefill with per-token request ids and positions).
+ *
+ * q, out [total_q][num_q_heads][head_dim] bf16, contiguous.  Rows
+ * cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 are request r's new tokens, at
+ * positions seq_lens[r] - (cu_seqlens_q[r+1] - cu_seqlens_q[r]) + local
+ * offset (seq_lens counts the new tokens); rows >= cu_seqlens_q[num_reqs]
+ * are padding and get 0.  Same math and limits as msa_sparse_decode;
+ * kv_dtype must be MSA_BF16 today.
+ */
+MSA_API msa_status_t msa_sparse_prefill(
+    const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,
+    const msa_kv_cache_t* kv,
+    const int32_t* topk, int64_t topk_row_stride, int32_t topk_k,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t bt_cols, int32_t num_reqs,
+    const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+    float softmax_scale, void* out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Scatter index keys into the key-only side cache.
+ * [SPA] minimax_m3_insert_index_cache: keys [N, D] into a cache [B, T, D]
+ * through a length-N slot mapping; empty input returns at once; the cache's
+ * last dimension must be contiguous.  Slot s (int64) goes to block s / T,
+ * position s % T; negative slots (padding) and slots >= B*T are skipped.
+ * dtype gives the element size (MSA_BF16 / MSA_FP16: 2 bytes, MSA_FP32: 4,
+ * MSA_FP8_E4M3FN: 1); strides are in elements.
+ */
+MSA_API msa_status_t msa_insert_index_cache(
+    const void* index_k, int64_t k_stride0, int64_t k_stride1, int32_t n, int32_t d, int32_t dtype,
+    void* index_cache, int64_t c_stride0, int64_t c_stride1, int64_t c_stride2,
+    int32_t num_blocks, int32_t cache_block_size,
+    const int64_t* slot_mapping, int64_t slot_stride, hipStream_t stream);
+
+/*
+ * Test hook: the dequantized K and V of n tokens, through the same device
+ * conversions the attends use.  pages [n], slots [n] int32 (page id and
+ * token 0..15 within it); k_out, v_out [n][num_kv_heads][head_dim] fp32 =
+ * stored value (bf16 / fp8 / e2m1 x block scale) x k_scale or v_scale,
+ * rounded to nearest fp32.  V is read at page + (block_page_stride - 8)
+ * for bf16 / fp8.  Tokens whose page is outside [0, num_pages) give NaN.
+ */
+MSA_API msa_status_t msa_debug_dequant_tokens(
+    const msa_kv_cache_t* kv, const int32_t* pages, const int32_t* slots, int32_t n,
+    float* k_out, float* v_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -33,3 +33,36 @@ def oracle_positions(wl):
 
 def q_f64(q):
     return q.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rows_blocks(wl, rows, pos, req):
+    """Physical blocks the oracle's masks of `rows` touch."""
+    need = set()
+    for i in rows:
+        toks = oracle.token_mask(wl.topk[i], int(pos[i]), wl.block_table.shape[1])
+        for b in set((toks // 128).tolist()):
+            need.add(int(wl.block_table[req[i], b]))
+    return sorted(need)
+
+
+def compact_oracle_inputs(wl, cache, rows):
+    """Oracle cache holding only the blocks `rows` read, plus a remapped block table.
+
+    The pages of each needed physical block (all block_page_stride of them, so
+    V pages of a packed layout come along) are copied from the device in one
+    gather; block ids are renumbered densely.  Attention is invariant to that
+    renumbering (pinned in the oracle tests).
+    """
+    req, pos = oracle_positions(wl)
+    need = rows_blocks(wl, rows, pos, req)
+    stride = wl.block_page_stride
+    remap = np.zeros(wl.num_phys_blocks, dtype=np.int64)
+    remap[need] = np.arange(len(need))
+    page_idx = (np.asarray(need, dtype=np.int64)[:, None] * stride + np.arange(stride)[None, :]).reshape(-1)
+    idx = torch.from_numpy(page_idx).to(cache["k_pages"].device)
+    small = dict(cache)
+    small["k_pages"] = cache["k_pages"].index_select(0, idx)
+    if cache["v_pages"] is not None:
+        small["v_pages"] = cache["v_pages"].index_select(0, idx)
+    bt = remap[wl.block_table]
+    return oracle_cache(wl, small), bt, req, pos

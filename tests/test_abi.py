@@ -1,0 +1,122 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/msa.h
+declares, and rejects bad arguments before touching the GPU (no kernel runs:
+each call below fails validation, which precedes any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_paged_query_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(msa.library_path()), reason="libmsa.so not built")
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MSA_API\s+[\w\s\*]+?\b(msa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ["msa_build_sparse_block_table", "msa_sparse_decode", "msa_sparse_prefill",
+              "msa_insert_index_cache", "msa_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(msa.library_path())
+    for n in declared():
+        assert hasattr(lib, n), n
+
+
+def _lib():
+    return msa.load_library()
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _table(**kw):
+    args = dict(topk=FAKE, topk_row_stride=4, topk_k=4, total_q=3, block_table=FAKE, bt_row_stride=8, bt_cols=8,
+                num_reqs=2, seq_lens=FAKE, dql=1, req_id=None, abs_pos=None, bps=8, sbt=FAKE, sbt_stride=32,
+                ctx=FAKE)
+    args.update(kw)
+    return _lib().msa_build_sparse_block_table(*args.values(), None)
+
+
+def test_table_rejects_row_count_mismatch():
+    # the decode builder's assertion: rows must equal batch * decode_query_len
+    assert _table(total_q=3, num_reqs=2, dql=1) == 1     # MSA_ERR_INVALID_ARGUMENT
+    assert b"batch * decode_query_len" in _lib().msa_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(topk_k=0), 2), (dict(topk_k=5000), 2), (dict(topk_row_stride=2), 1), (dict(bt_row_stride=4), 1),
+    (dict(sbt_stride=16), 1), (dict(req_id=FAKE), 1), (dict(dql=0, total_q=0), 1), (dict(bps=0), 1),
+])
+def test_table_argument_errors(kw, status):
+    assert _table(**kw) == status
+
+
+def test_empty_inputs_are_noops():
+    assert _table(total_q=0, num_reqs=0) == 0
+    assert _lib().msa_insert_index_cache(FAKE, 1, 1, 0, 128, 0, FAKE, 1, 1, 1, 4, 16, FAKE, 1, None) == 0
+
+
+def test_index_cache_needs_contiguous_head_dim():
+    st = _lib().msa_insert_index_cache(FAKE, 128, 1, 5, 128, 0, FAKE, 128 * 16, 128, 2, 4, 16, FAKE, 1, None)
+    assert st == 1 and b"contiguous head dimension" in _lib().msa_last_error()
+
+
+def _kv(**kw):
+    d = dict(kv_dtype=msa.MSA_BF16, num_kv_heads=8, head_dim=128, block_page_stride=8, k_pages=0x1000,
+             v_pages=0x2000, page_stride_bytes=8 * 16 * 128 * 2, num_pages=64, k_scale=None, v_scale=None)
+    d.update(kw)
+    return msa._KV(*d.values())
+
+
+def _decode(kv, **kw):
+    args = dict(q=FAKE, q_dtype=0, num_reqs=4, dql=1, hq=64, kv=ctypes.byref(kv), topk=FAKE, topk_stride=16,
+                topk_k=16, bt=FAKE, bt_stride=64, bt_cols=64, seq=FAKE, scale=0.1, out=FAKE, ws=None, ws_bytes=0)
+    args.update(kw)
+    return _lib().msa_sparse_decode(*args.values(), None)
+
+
+@pytest.mark.parametrize("kvkw,kw,status", [
+    (dict(head_dim=96), {}, 2),
+    (dict(kv_dtype=msa.MSA_NVFP4, head_dim=64, page_stride_bytes=2 * 8 * 9 * 64), {}, 2),
+    (dict(kv_dtype=7), {}, 2),
+    ({}, dict(hq=60), 1),
+    ({}, dict(hq=8 * 32), 2),
+    (dict(block_page_stride=12), {}, 1),
+    (dict(page_stride_bytes=100), {}, 1),
+    ({}, dict(q_dtype=msa.MSA_FP16), 2),
+    ({}, dict(topk_k=2048), 2),
+    ({}, dict(q=ctypes.c_void_p(0x1001)), 1),
+    ({}, dict(scale=float("nan")), 1),
+])
+def test_decode_argument_errors(kvkw, kw, status):
+    assert _decode(_kv(**kvkw), **kw) == status
+
+
+def test_decode_empty_batch_is_noop():
+    assert _decode(_kv(), num_reqs=0) == 0
+
+
+def test_prefill_rejects_fp8_pages():
+    kv = _kv(kv_dtype=msa.MSA_FP8_E4M3FN, page_stride_bytes=8 * 16 * 128)
+    st = _lib().msa_sparse_prefill(FAKE, 0, 10, 64, ctypes.byref(kv), FAKE, 16, 16, FAKE, 64, 64, 1, FAKE, FAKE,
+                                   0.1, FAKE, None, 0, None)
+    assert st == 2
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(msa, "_lib", None)
+    monkeypatch.setattr(msa, "library_path", lambda: str(tmp_path / "libmsa.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        msa.load_library()

@@ -1,0 +1,224 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: sparse block table, context lengths, prefill positions, dequant
+hook, index-cache insert.  Attention: max |GPU - oracle| <= 1e-2 (the bound
+the method's acceptance states for bf16 outputs on N(0, 1) inputs), with
+every unread byte of the cache NaN-poisoned.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_sparse_paged_query_amd as msa
+from synth import make_workload, make_kv_cache, make_query, written_blocks
+from tests.helpers import compact_oracle_inputs, oracle_cache, oracle_positions, q_f64
+
+pytestmark = pytest.mark.gpu
+ATOL = 1e-2
+DEV = "cuda"
+
+
+def _dev(x, dtype=torch.int32):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV, dtype)
+
+
+def _kv(wl, cache):
+    ks = vs = None
+    if wl.kv_dtype != "bf16":
+        ks = torch.tensor([cache["k_scale"]], dtype=torch.float32, device=DEV)
+        vs = torch.tensor([cache["v_scale"]], dtype=torch.float32, device=DEV)
+    return msa.KVCache(wl.kv_dtype, cache["k_pages"], cache["v_pages"], wl.num_kv_heads, wl.head_dim,
+                       wl.block_page_stride, ks, vs)
+
+
+def _run(wl, cache, q):
+    kv = _kv(wl, cache)
+    topk, bt, seq = _dev(wl.topk), _dev(wl.block_table), _dev(wl.seq_lens)
+    if wl.mode == "decode":
+        out = msa.msa_sparse_decode(q, kv, topk, bt, seq, wl.softmax_scale, decode_query_len=wl.decode_query_len)
+    else:
+        out = msa.msa_sparse_prefill(q, kv, topk, bt, _dev(wl.cu_seqlens_q), seq, wl.softmax_scale)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------- tables
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C5", "C2s", "C3s"])
+@pytest.mark.parametrize("stride", [8, 16])
+def test_decode_table_bit_exact(name, stride):
+    wl = make_workload(name)
+    req, pos = oracle.decode_positions(wl.seq_lens, wl.decode_query_len)
+    want_bt, want_ctx = oracle.sparse_block_table(wl.topk, wl.block_table, req, pos, stride)
+    sbt, ctx = msa.msa_build_sparse_block_table(_dev(wl.topk), _dev(wl.block_table), seq_lens=_dev(wl.seq_lens),
+                                                decode_query_len=wl.decode_query_len, block_page_stride=stride)
+    assert (sbt.cpu().numpy() == want_bt).all()
+    assert (ctx.cpu().numpy() == want_ctx).all()
+
+
+@pytest.mark.parametrize("name", ["C4", "C4s"])
+def test_prefill_positions_and_table_bit_exact(name):
+    wl = make_workload(name)
+    req, pos = oracle.prefill_positions(wl.cu_seqlens_q, wl.seq_lens, wl.total_q)
+    qlen = np.diff(wl.cu_seqlens_q)
+    g_req, g_pos = msa.msa_query_token_positions(_dev(wl.cu_seqlens_q), _dev(wl.seq_lens - qlen), wl.total_q)
+    assert (g_req.cpu().numpy() == req).all() and (g_pos.cpu().numpy() == pos).all()
+    want_bt, want_ctx = oracle.sparse_block_table(wl.topk, wl.block_table, req, pos)
+    sbt, ctx = msa.msa_build_sparse_block_table(_dev(wl.topk), _dev(wl.block_table), query_req_id=_dev(req),
+                                                query_abs_pos=_dev(pos))
+    assert (sbt.cpu().numpy() == want_bt).all()
+    assert (ctx.cpu().numpy() == want_ctx).all()
+    if name == "C4":
+        assert int(ctx.sum()) == 36_842_496
+
+
+def test_table_edge_rows():
+    # hand rows around block edges, future ids, ids past the table, padding
+    bt = np.array([[9, 3, 12, 0, 7, 1, 13, 4]], dtype=np.int32)
+    topk = np.array([[5, 7, -1, 2], [8, 7, 3, 1], [0, -1, -1, -1], [1, 0, -1, -1], [3, 0, 2, 1],
+                     [5, 7, -1, 2], [9, 40, -1, -1]], dtype=np.int32)
+    pos = np.array([999, 999, 127, 128, 0, -1, 1023], dtype=np.int32)
+    req = np.zeros(len(pos), dtype=np.int32)
+    want_bt, want_ctx = oracle.sparse_block_table(topk, bt, req, pos)
+    sbt, ctx = msa.msa_build_sparse_block_table(_dev(topk), _dev(bt), query_req_id=_dev(req), query_abs_pos=_dev(pos))
+    assert (sbt.cpu().numpy() == want_bt).all() and (ctx.cpu().numpy() == want_ctx).all()
+
+
+# ---------------------------------------------------------------- dequant
+
+def _hook_vs_oracle(wl, cache, pages, slots):
+    kv = _kv(wl, cache)
+    k, v = msa.msa_debug_dequant_tokens(kv, _dev(pages), _dev(slots))
+    oc = oracle_cache(wl, cache)
+    wk = oc.read_tokens("k", pages, slots).astype(np.float32)
+    wv = oc.read_tokens("v", pages, slots).astype(np.float32)
+    for got, want in ((k.cpu().numpy(), wk), (v.cpu().numpy(), wv)):
+        nan = np.isnan(want)
+        assert (np.isnan(got) == nan).all()
+        assert (got[~nan].view(np.uint32) == want[~nan].view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("name", ["C3s", "C5s", "C2s"])
+def test_dequant_hook_bit_exact_on_written_tokens(name):
+    wl = make_workload(name)
+    cache = make_kv_cache(wl, DEV)
+    pages, slots = [], []
+    for (r, b, n) in written_blocks(wl):
+        phys = int(wl.block_table[r, b])
+        for t in range(n):
+            pages.append(phys * wl.block_page_stride + t // 16)
+            slots.append(t % 16)
+    _hook_vs_oracle(wl, cache, np.array(pages), np.array(slots))
+
+
+def test_dequant_hook_exhaustive_codes():
+    # fp8: all 256 codes; NVFP4: all 16 x 256 (code, scale) pairs, NaN scales included
+    wl = make_workload("C1", kv_dtype="fp8", Hq=1, Hkv=1, D=128)
+    codes = torch.arange(256, dtype=torch.uint8, device=DEV).repeat(8).view(1, 1, 16, 128)
+    cache = dict(k_pages=codes.clone(), v_pages=codes.flip(-1).contiguous(), k_scale=0.75, v_scale=1.0 / 3.0,
+                 page_stride_bytes=2048, num_pages=1)
+    cache["v_scale"] = float(np.float32(cache["v_scale"]))
+    _hook_vs_oracle(wl, cache, np.zeros(16, dtype=np.int64), np.arange(16))
+    wl4 = make_workload("C1", kv_dtype="nvfp4", Hq=1, Hkv=1, D=128)
+    pages = torch.zeros((2, 2, 9 * 128), dtype=torch.uint8)
+    nib = torch.arange(16, dtype=torch.uint8)
+    for p in range(2):
+        for s in range(2):
+            data = (nib.repeat(16 * 8)[0::2] | (nib.repeat(16 * 8)[1::2] << 4)).view(16, 64)
+            pages[p, s, :1024] = torch.roll(data.reshape(-1), shifts=s)
+            pages[p, s, 1024:] = torch.arange(128, dtype=torch.uint8) + 128 * p
+    cache4 = dict(k_pages=pages.to(DEV), v_pages=None, k_scale=float(np.float32(0.0123)),
+                  v_scale=float(np.float32(3.5)), page_stride_bytes=2 * 9 * 128, num_pages=2)
+    pg = np.repeat(np.arange(2), 16)
+    sl = np.tile(np.arange(16), 2)
+    _hook_vs_oracle(wl4, cache4, pg, sl)
+
+
+# ---------------------------------------------------------------- attention
+
+def _parity(wl, rows=None):
+    cache = make_kv_cache(wl, DEV)
+    q = make_query(wl, DEV)
+    out = _run(wl, cache, q)
+    req, pos = oracle_positions(wl)
+    rows = np.arange(wl.total_q) if rows is None else np.asarray(rows)
+    oc, bt, _, _ = compact_oracle_inputs(wl, cache, rows)
+    qf = np.zeros((wl.total_q, wl.num_q_heads, wl.head_dim))   # only sampled rows are read
+    qf[rows] = q_f64(q[torch.from_numpy(rows).to(DEV)])
+    want = oracle.sparse_attention(qf, oc, wl.topk, bt, req, pos, wl.softmax_scale, rows=rows)
+    got = out.float().cpu().numpy()[rows]
+    assert np.isfinite(got).all()
+    err = np.abs(got - want).max()
+    assert err <= ATOL, f"max abs error {err}"
+    return out, err
+
+
+@pytest.mark.parametrize("name", ["C1", "C2s", "C3s", "C5s"])
+def test_decode_parity_small(name):
+    _parity(make_workload(name))
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s"])
+def test_decode_parity_stride16(name):
+    _parity(make_workload(name, block_page_stride=16))
+
+
+def test_decode_dql_and_head_dim_variants():
+    # multi-token decode at head_dim 64 with GQA 2, and bf16 at dql 3
+    _parity(make_workload("C3s", D=64, Hq=16, Hkv=8, k=8, seed=31))
+    _parity(make_workload("C2s", dql=3, Hq=32, Hkv=2, seed=32))
+
+
+def test_prefill_parity_small():
+    _parity(make_workload("C4s"))
+
+
+@pytest.mark.parametrize("name,rows", [
+    ("C2", [0, 17, 33, 63]),
+    ("C3", [0, 1, 2, 3, 70, 127]),
+    ("C5", [0, 64, 127]),
+])
+def test_decode_parity_full_size_sampled(name, rows):
+    _parity(make_workload(name), rows)
+
+
+def test_prefill_parity_full_size_sampled():
+    wl = make_workload("C4")
+    rows = [0, 127, 128, 2047, 2048, 6000, 14335, 14336, 22527, 22528, 22591]
+    _parity(wl, rows)
+
+
+def test_decode_deterministic():
+    wl = make_workload("C3s")
+    cache = make_kv_cache(wl, DEV)
+    q = make_query(wl, DEV)
+    a = _run(wl, cache, q)
+    b = _run(wl, cache, q)
+    assert torch.equal(a, b)
+
+
+def test_empty_context_rows_are_zero():
+    # a decode row whose every id is in the future or padding attends nothing
+    wl = make_workload("C2s")
+    wl.topk[1] = -1
+    wl.topk[2] = np.array([10_000] * wl.topk_k)
+    out, _ = _parity(wl)
+    assert (out[1].float() == 0).all() and (out[2].float() == 0).all()
+
+
+# ---------------------------------------------------------------- index cache
+
+def test_index_cache_insert_bit_exact():
+    g = torch.Generator().manual_seed(5)
+    N, B, T, D = 300, 12, 64, 128
+    k = torch.randn(N, D, generator=g).to(torch.bfloat16)
+    cache = torch.randn(B, T, D, generator=g).to(torch.bfloat16)
+    slots = torch.randperm(B * T, generator=g)[:N].to(torch.int64)
+    slots[::7] = -1
+    want = oracle.insert_index_cache(k.float().numpy(), cache.float().numpy().copy(), slots.numpy())
+    gc = cache.to(DEV)
+    msa.msa_insert_index_cache(k.to(DEV), gc, slots.to(DEV))
+    torch.cuda.synchronize()
+    assert (gc.float().cpu().numpy() == want).all()
