@@ -226,6 +226,11 @@ def encode_nvfp4_rows(x, global_scale):
     return packed, s_code.view(torch.uint8)
 
 
+def _f32(x):
+    """Round a python float to the nearest fp32 value (scales are fp32 scalars)."""
+    return float(np.float32(x))
+
+
 def make_kv_cache(wl, device="cpu"):
     """Allocate and fill the paged cache of a workload.
 
@@ -246,9 +251,8 @@ def make_kv_cache(wl, device="cpu"):
     gen.manual_seed(wl.seed * 1000 + 2)
     K = torch.randn((nb, BLOCK, Hkv, D), generator=gen, device=device, dtype=torch.float32)
     V = torch.randn((nb, BLOCK, Hkv, D), generator=gen, device=device, dtype=torch.float32)
-    present = torch.zeros((nb, BLOCK), dtype=torch.bool, device=device)
-    for i, (_, _, n) in enumerate(wb):
-        present[i, :n] = True
+    n_tok = torch.tensor([n for (_, _, n) in wb], dtype=torch.int64, device=device)
+    present = torch.arange(BLOCK, device=device)[None, :] < n_tok[:, None]
     phys = torch.tensor([int(wl.block_table[r, b]) for (r, b, _) in wb], dtype=torch.int64, device=device)
     pm = present[:, :, None, None]
     k_scale = v_scale = 1.0
@@ -258,13 +262,13 @@ def make_kv_cache(wl, device="cpu"):
         Vc = V.to(torch.bfloat16).view(torch.uint8).reshape(nb, BLOCK, Hkv, D * 2)
     elif wl.kv_dtype == "fp8":
         esize = 1
-        k_scale = float(K.abs().amax(dim=(2, 3))[present].max()) / 448.0 if nb else 1.0
-        v_scale = float(V.abs().amax(dim=(2, 3))[present].max()) / 448.0 if nb else 1.0
+        k_scale = _f32(float(K.abs().amax(dim=(2, 3))[present].max()) / 448.0) if nb else 1.0
+        v_scale = _f32(float(V.abs().amax(dim=(2, 3))[present].max()) / 448.0) if nb else 1.0
         Kc = encode_fp8_e4m3fn(K, k_scale)
         Vc = encode_fp8_e4m3fn(V, v_scale)
     else:
-        k_scale = float(K.abs().amax(dim=(2, 3))[present].max()) / (6.0 * 448.0) if nb else 1.0
-        v_scale = float(V.abs().amax(dim=(2, 3))[present].max()) / (6.0 * 448.0) if nb else 1.0
+        k_scale = _f32(float(K.abs().amax(dim=(2, 3))[present].max()) / (6.0 * 448.0)) if nb else 1.0
+        v_scale = _f32(float(V.abs().amax(dim=(2, 3))[present].max()) / (6.0 * 448.0)) if nb else 1.0
         kd, ks = encode_nvfp4_rows(K, k_scale)
         vd, vs = encode_nvfp4_rows(V, v_scale)
     if wl.kv_dtype in ("bf16", "fp8"):
