@@ -81,6 +81,99 @@ def _cpu_baseline(wl, cache, q, ctx, seconds):
             "sample": f"{done} of {wl.total_q} rows (random, non-empty), {elapsed:.1f} s of fp64 numpy"}
 
 
+KERNEL_SOURCES = {
+    "decode": ["attend_rows.hip", "msa_device.h", "msa_internal.h"],
+    "prefill": ["prefill.hip", "msa_device.h", "msa_internal.h"],
+}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash(mode):
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_paged_query_amd", "csrc")
+    for f in KERNEL_SOURCES[mode]:
+        p = os.path.join(csrc, f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(config, mode):
+    """HBM bytes per launch from a committed counter summary of this config,
+    if it was taken on the current kernel sources; else None."""
+    if not os.path.isdir(PROFILES):
+        return None
+    want = kernel_source_hash(mode)
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith(".md"):
+            continue
+        for ln in open(os.path.join(PROFILES, name)):
+            if ln.startswith("<!-- traffic-json: "):
+                d = json.loads(ln[len("<!-- traffic-json: "):].rsplit("-->", 1)[0])
+                if d.get("config") == config and d.get("source_hash") == want:
+                    return d.get("traffic_bytes")
+    return None
+
+
+def _read_csv(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize(args):
+    """Write profiles/<name>.md from rocprofv3 outputs (kernel trace + two counter runs + copy calibration)."""
+    import numpy as np
+    mode = "prefill" if args.config == "C4" else "decode"
+    key = args.kernel
+    stats = [r for r in _read_csv(args.trace_dir) if "Calls" in r and key in r["Name"]]
+    trace = [r for r in _read_csv(args.trace_dir) if "Start_Timestamp" in r and key in r.get("Kernel_Name", "")]
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace]
+
+    def counter(d, name, kern):
+        return [float(r["Counter_Value"]) for r in _read_csv(d)
+                if r.get("Counter_Name") == name and kern in r.get("Kernel_Name", "")]
+    fetch = counter(args.fetch_dir, "FETCH_SIZE", key)
+    write = counter(args.write_dir, "WRITE_SIZE", key)
+    cfetch = counter(args.copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cwrite = counter(args.copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    copy_kib = args.copy_mib * 1024.0
+    fscale = copy_kib / float(np.median(cfetch))
+    wscale = copy_kib / float(np.median(cwrite))
+    fetch_b = float(np.median(fetch)) * 1024 * fscale
+    write_b = float(np.median(write)) * 1024 * wscale
+    info = {"config": args.config, "kernel": key, "source_hash": kernel_source_hash(mode),
+            "avg_ns": float(np.mean(durs)), "dispatches": len(durs),
+            "fetch_kib_raw": float(np.median(fetch)), "write_kib_raw": float(np.median(write)),
+            "fetch_scale": fscale, "write_scale": wscale,
+            "traffic_bytes": fetch_b + write_b}
+    lines = [f"# {key}: {args.config} ({DESCR[args.config]})", "",
+             "Commands (run from the repository root on one MI355X; rocprofv3 writes CSVs):", "",
+             "```", *args.commands.split(" ;; "), "```", "",
+             f"* kernel dispatches traced: {len(durs)}; average duration {np.mean(durs) / 1e3:.2f} us "
+             f"(min {min(durs) / 1e3:.2f}, max {max(durs) / 1e3:.2f})",
+             f"* FETCH_SIZE per dispatch (median): {info['fetch_kib_raw']:.1f} KiB raw x {fscale:.4f} "
+             f"= {fetch_b / 1e6:.2f} MB",
+             f"* WRITE_SIZE per dispatch (median): {info['write_kib_raw']:.1f} KiB raw x {wscale:.4f} "
+             f"= {write_b / 1e6:.2f} MB",
+             f"* copy calibration: a {args.copy_mib} MiB device copy reads {np.median(cfetch):.1f} KiB "
+             f"(FETCH_SIZE) and writes {np.median(cwrite):.1f} KiB (WRITE_SIZE)",
+             "", "Kernel statistics (rocprofv3 --stats), top entries:", "", "| kernel | calls | avg us | % |",
+             "|---|---|---|---|"]
+    allstats = sorted([r for r in _read_csv(args.trace_dir) if "Calls" in r and r["Name"] != "KERNEL_DISPATCH"],
+                      key=lambda r: -float(r["TotalDurationNs"]))[:8]
+    for r in allstats:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {r['Percentage']} |")
+    lines += ["", f"<!-- traffic-json: {json.dumps(info)} -->", ""]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(info))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +183,22 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 3 device-to-device copies of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--summarize", action="store_true", help="write a profiles/ summary from rocprofv3 CSVs")
+    ap.add_argument("--kernel", default="attend_rows_kernel")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--commands", default="")
+    ap.add_argument("--out")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -102,6 +210,15 @@ def main():
     from synth import make_kv_cache, make_query, make_workload
 
     dev = "cuda"
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
     wl = make_workload(args.config)
     print(f"[bench] {args.config}: building inputs", file=sys.stderr, flush=True)
     cache = make_kv_cache(wl, dev)
@@ -168,13 +285,13 @@ def main():
         value, unit = work / (ms_per_step * 1e-3) / 1e9, "GB/s"
         achieved = work / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(args.config, "decode")}
         dtype = "f16" if wl.kv_dtype == "nvfp4" else "bf16"
     else:
         value, unit = work / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
         achieved = work / (kernel_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(args.config, "prefill")}
         dtype = "bf16"
     cpu = None
     if not args.no_cpu_baseline:
