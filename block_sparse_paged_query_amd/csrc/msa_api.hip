@@ -244,6 +244,7 @@ MSA_API msa_status_t msa_sparse_decode(const void* q, int32_t q_dtype, int32_t n
   a.seq_lens = seq_lens;
   a.dql = decode_query_len;
   a.num_reqs = num_reqs;
+  a.total_rows = rows;
   int ns = choose_splits(rows, kv->num_kv_heads, topk_k, device_cus());
   while (ns > 1 && (workspace == nullptr || split_bytes(rows, num_q_heads, kv->head_dim, ns) > workspace_bytes)) --ns;
   a.nsplit = ns;
@@ -289,6 +290,9 @@ MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t 
   a.cu_seqlens_q = cu_seqlens_q;
   a.num_reqs = num_reqs;
   a.dql = 1;
+  a.total_rows = total_q;
+  if (msa::prefill_blocks_supported(a.group, kv->head_dim, fmt_of(kv->kv_dtype), bt_cols))
+    return hip_status(msa::launch_prefill_blocks(a, stream), "prefill launch");
   return hip_status(msa::launch_attend_rows(a, fmt_of(kv->kv_dtype), msa::kModePrefill, total_q, stream),
                     "prefill launch");
 }

@@ -175,6 +175,18 @@ def test_prefill_parity_small():
     _parity(make_workload("C4s"))
 
 
+@pytest.mark.parametrize("kw", [
+    dict(Hq=32, Hkv=2, seed=41),                         # 16 query heads per kv head
+    dict(Hq=16, Hkv=4, seed=42),                         # 4 per kv head: row-wise path
+    dict(D=64, Hq=16, Hkv=2, seed=43),                   # head_dim 64: row-wise path
+    dict(block_page_stride=16, seed=44),                 # K and V sides in one block
+    dict(qlens=[1, 40, 700], context=[3000, 0, 129], seed=45),   # long context, tiny request
+    dict(qlens=[0, 300], context=[50, 0], seed=46),      # an empty request
+])
+def test_prefill_parity_variants(kw):
+    _parity(make_workload("C4s", **kw))
+
+
 @pytest.mark.parametrize("name,rows", [
     ("C2", [0, 17, 33, 63]),
     ("C3", [0, 1, 2, 3, 70, 127]),
