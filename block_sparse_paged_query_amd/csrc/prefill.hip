@@ -16,14 +16,14 @@
 // selected it (and may see it causally), then walks the blocks some row
 // selected in ascending order.  Each such block's K and V (128 keys x 256 B)
 // go once into LDS by direct global-to-LDS loads (each lane's LDS slot is
-// fixed, so layouts are made by choosing which global chunk a lane fetches):
-// K double-buffered as [key][d] with 16-byte chunks XOR-swizzled by key, V
-// as plain [key][d].  At each block boundary, while no copy is in flight, V
-// is transposed LDS-to-LDS (8 keys x 8 d per thread, in registers) into V^T
-// cells: for each 32-key chunk and d, the 8 keys of a lane group in the order
-// the P operand holds them, placed so that both the transposing writes and
-// the operand reads are free of bank conflicts.  Both operands are then plain
-// 16-byte LDS reads, and the next block's copies overlap the compute.  Every
+// fixed, so layouts are made by choosing which global chunk a lane fetches),
+// double-buffered: K as [key][d] with 16-byte chunks XOR-swizzled by key, V
+// as [d pair of 16-byte chunks][key] so that the transposing read
+// ds_read_b64_tr_b16 (a lane receives one column of the 4 key rows its
+// 16-lane group points at) yields the V^T operand with no bank conflict.
+// The next block's copies are issued in four pieces, one after each 32-key
+// chunk's V reads; the compiler waits for outstanding copies before a
+// transposing read, so each piece has one chunk of compute to land.  Every
 // wave
 // owns 2 matrix tiles of 16 rows = (16 / G query rows) x (G heads) and runs
 // QK^T and PV only for the tiles whose rows selected the block; the other
@@ -54,61 +54,44 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // K row swizzle: 16-byte chunk c of key row k sits at chunk c ^ (k & 15).
 __device__ __forceinline__ int k_swz(int key) { return key & 15; }
 
-// V^T cell of (d, key group g) inside an 8 KB chunk: row (d/16, g) of 256 B,
-// 16-byte cell (d % 16) ^ (d / 16).  Reads (16 lanes: d = 16 nn + r) and the
-// transposing writes (16 lanes: d = 8 m + e) each touch 16 distinct cells of
-// one 256-byte row or of distinct bank groups.
-__device__ __forceinline__ int vt_cell(int d, int g) {
-  return (((d >> 4) * 4 + g) << 8) + ((((d & 15) ^ (d >> 4)) & 15) << 4);
-}
-
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// K and V of block `phys` (logical block `blk`), kv head kvh, into LDS: 4 + 4
-// direct 16-byte loads per lane.  Keys at or past seq_len are read from key 0
-// of the block instead (finite data that gets probability zero), so no NaN
-// of an unwritten slot reaches the products.
-__device__ __forceinline__ void pf_issue_block(lds_u8* kb, lds_u8* vb, const AttendArgs& a, int kvh, int phys,
-                                               int blk, int seq_len) {
+// V layout: 16-byte slot ((lc / 2) * 128 + key) * 2 + lc % 2 holds chunk lc
+// (d = 8 lc .. 8 lc + 7) of key.
+
+// Piece `part` (0..3) of the copy of block `phys` (logical block `blk`), kv
+// head kvh, into LDS (kb, vb): one 16-byte K load and one V load per lane.
+// K unit (wave, part) holds keys 16 wave + 4 part + lane / 16 (one page per
+// wave), V unit holds keys 32 part + lane / 2 (two pages) at d chunk
+// 2 wave + lane % 2, so the addresses are a per-block scalar base plus a small
+// per-lane constant.  Keys at or past seq_len (only in a request's last
+// block) are read from key 0 of the block instead (finite data that gets
+// probability zero), so no NaN of an unwritten slot reaches the products.
+__device__ __forceinline__ void pf_issue_part(lds_u8* kb, lds_u8* vb, const AttendArgs& a, int kvh, int phys,
+                                              int blk, int seq_len, int part) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t pg = (int64_t)phys * a.block_page_stride;
   const int64_t head_off = (int64_t)kvh * kPageTokens * 256;
   const int nkeys = seq_len - blk * kBlockTokens;     // keys of this block that exist (>= 1)
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int P = (wave * 4 + s) * 1024 + lane * 16;  // LDS byte this lane fills
-    const int key = P >> 8, pc = (P >> 4) & 15;
-    const int src = key < nkeys ? key : 0;
-    const int64_t row = (src >> 4) * a.page_stride + head_off + (src & 15) * 256;
-    __builtin_amdgcn_global_load_lds(a.k_base + pg * a.page_stride + row + ((pc ^ k_swz(key)) << 4),
-                                     kb + (wave * 4 + s) * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(a.v_base + (pg + a.v_page_offset) * a.page_stride + row + (pc << 4),
-                                     vb + (wave * 4 + s) * 1024, 16, 0, 0);
-  }
-}
-
-// V [key][d] -> V^T cells.  Wave w handles 32-key chunk c = w / 2; lane
-// (g, ml) of it takes keys tau(8g .. 8g+7) of the chunk (4g..4g+3 and
-// 16+4g..16+4g+3) and d = 4m .. 4m+3 with m = 16 (w % 2) + ml.
-__device__ __forceinline__ void pf_transpose_v(const uint8_t* vnat, uint8_t* vt) {
-  const int tid = threadIdx.x, wave = tid >> 6, c = wave >> 1;
-  const int g = (tid >> 4) & 3, m = 16 * (wave & 1) + (tid & 15);
-  u32x2 v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int key = c * 32 + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
-    v[i] = *reinterpret_cast<const u32x2*>(vnat + key * 256 + m * 8);
-  }
-  uint8_t* vc = vt + c * 8192;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a0 = v[2 * p][e >> 1], a1 = v[2 * p + 1][e >> 1];
-      o[p] = (e & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
-    }
-    *reinterpret_cast<u32x4*>(vc + vt_cell(4 * m + e, g)) = o;
+  const int unit = wave * 4 + part;                   // 1 KB unit of the 32 KB block this wave fills
+  const int kkey = 16 * wave + 4 * part + (lane >> 4), kpc = lane & 15;
+  const int vkey = 32 * part + (lane >> 1), vlc = 2 * wave + (lane & 1);
+  if (nkeys >= kBlockTokens && a.page_stride < (int64_t(1) << 30)) {
+    const uint8_t* kbase = a.k_base + (pg + wave) * a.page_stride + head_off;
+    const uint8_t* vbase = a.v_base + (pg + a.v_page_offset + 2 * part) * a.page_stride + head_off;
+    const uint32_t koff = (uint32_t)((kkey & 15) * 256 + ((kpc ^ k_swz(kkey)) << 4));
+    const uint32_t voff = (uint32_t)((lane >> 5) * a.page_stride + (vkey & 15) * 256 + (vlc << 4));
+    __builtin_amdgcn_global_load_lds(kbase + koff, kb + unit * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + voff, vb + unit * 1024, 16, 0, 0);
+  } else {
+    const int ks = kkey < nkeys ? kkey : 0, vs = vkey < nkeys ? vkey : 0;
+    __builtin_amdgcn_global_load_lds(a.k_base + (pg + (ks >> 4)) * a.page_stride + head_off + (ks & 15) * 256 +
+                                         ((kpc ^ k_swz(kkey)) << 4),
+                                     kb + unit * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a.v_base + (pg + a.v_page_offset + (vs >> 4)) * a.page_stride + head_off +
+                                         (vs & 15) * 256 + (vlc << 4),
+                                     vb + unit * 1024, 16, 0, 0);
   }
 }
 
@@ -116,99 +99,158 @@ struct PfWave {
   static constexpr int KK = 4, NN = 8;
   bf16x8 qop[kPfTiles][KK];
   f32x4 acc[kPfTiles][NN];
-  float m[kPfTiles], l[kPfTiles];
+  f32x4 lacc[kPfTiles];   // softmax denominators: P times an all-ones operand
+  float m[kPfTiles];
   int lrow[kPfTiles];     // row within the workgroup tile, or -1
   int lpos[kPfTiles];     // that row's absolute position
 };
 
 // Online softmax keeps, per (row, head), a reference max m and rescales the
-// accumulators only when a chunk's max exceeds m by more than kLazy (log2
-// units): probabilities are then at most 2^kLazy, well inside bf16 / fp32
-// range, and the common case skips the rescale of 32 accumulators per tile.
+// accumulators only when some lane's chunk max exceeds m by more than kLazy
+// (log2 units): probabilities are then at most 2^kLazy, well inside bf16 /
+// fp32 range.  The common case needs no cross-lane max and no rescale; the
+// denominator is accumulated by the matrix core (P times a ones operand), so
+// it sums exactly the bf16 probabilities the PV product uses.
 constexpr float kLazy = 8.f;
+
+// One 32-key chunk against the tiles in MASK (a compile-time set, so that the
+// phases below form straight-line code): all QK^T products, then all
+// softmaxes (one uniform branch covers the rare rescale of any tile), then all
+// PV products.  A tile's softmax runs while the next tile's products are in
+// the matrix pipe, and its PV products while the next softmax runs.
+template <int MASK>
+__device__ __forceinline__ void pf_chunk(PfWave& w, const bf16x8 (&kop)[2][PfWave::KK], const bf16x8 (&vop)[PfWave::NN],
+                                         const float (&bias)[kPfTiles], const bf16x8& ones, float sl2, bool causal,
+                                         int kbase) {
+  constexpr int KK = PfWave::KK, NN = PfWave::NN;
+  float sv[kPfTiles][8];
+#pragma unroll
+  for (int i = 0; i < kPfTiles; ++i) {
+    if (!((MASK >> i) & 1)) continue;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s0 = mfma16(kop[0][kk], w.qop[i][kk], s0);
+      s1 = mfma16(kop[1][kk], w.qop[i][kk], s1);
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      sv[i][ii] = s0[ii];
+      sv[i][4 + ii] = s1[ii];
+    }
+  }
+  float mxs[kPfTiles];
+  bool need = false;
+#pragma unroll
+  for (int i = 0; i < kPfTiles; ++i) {
+    if (!((MASK >> i) & 1)) continue;
+    if (causal) {
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const int kp = kbase + (ii & 3) + ((ii >> 2) << 4);
+        sv[i][ii] = kp <= w.lpos[i] ? sv[i][ii] : -INFINITY;
+      }
+    }
+    float mx = sv[i][0];
+#pragma unroll
+    for (int ii = 1; ii < 8; ++ii) mx = fmaxf(mx, sv[i][ii]);
+    mxs[i] = fmaf(mx, sl2, bias[i]);                       // this lane's chunk max, scaled (log2 units)
+    need |= mxs[i] > w.m[i] + kLazy;
+  }
+  if (__ballot(need)) {                                    // rare after the first chunk of a row
+#pragma unroll
+    for (int i = 0; i < kPfTiles; ++i) {
+      if (!((MASK >> i) & 1)) continue;
+      float mh = fmaxf(mxs[i], __shfl_xor(mxs[i], 16));
+      mh = fmaxf(mh, __shfl_xor(mh, 32));                  // the head's chunk max
+      const float m_new = fmaxf(w.m[i], mh);
+      const float alpha = exp2_fast(w.m[i] - (m_new == -INFINITY ? 0.f : m_new));
+#pragma unroll
+      for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = w.acc[i][nn] * alpha;
+      w.lacc[i] = w.lacc[i] * alpha;
+      w.m[i] = m_new;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPfTiles; ++i) {
+    if (!((MASK >> i) & 1)) continue;
+    const float off = bias[i] - (w.m[i] == -INFINITY ? 0.f : w.m[i]);
+    float p[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) p[ii] = exp2_fast(fmaf(sv[i][ii], sl2, off));
+    const u32x4 pw = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = mfma16(vop[nn], pop, w.acc[i][nn]);
+    w.lacc[i] = mfma16(ones, pop, w.lacc[i]);
+  }
+}
+
+struct PfNext {       // the block whose copies are issued during this one
+  lds_u8* kb;
+  lds_u8* vb;
+  int phys, blk;
+  bool valid;
+};
 
 // One selected block against this wave's tiles.  `causal` is set when the
 // block can be the own block of a row of this workgroup (keys past a row's
 // position must be masked); earlier blocks need only the row selection.
-__device__ __forceinline__ void pf_compute_block(PfWave& w, const uint8_t* kb, const uint8_t* vtb, uint32_t bmask,
-                                                 int blk, int wave, int RT, float sl2, bool causal) {
+// Every wave issues its pieces of the next block's copies, active or not.
+__device__ __forceinline__ void pf_compute_block(PfWave& w, const uint8_t* kb, const uint8_t* vb, uint32_t bmask,
+                                                 int blk, int wave, int RT, float sl2, bool causal,
+                                                 const PfNext& nx, const AttendArgs& a, int kvh, int seq_len) {
   constexpr int KK = PfWave::KK, NN = PfWave::NN;
+  static_assert(kPfTiles == 2, "the tile sets below enumerate two tiles");
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   // per-lane LDS offsets (chunk / tile / step parts are compile-time)
   int koff[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) koff[kk] = r * 256 + (((4 * kk + g) ^ r) << 4);
-
-  // per-tile row selection: bias 0 for a selected row, -inf otherwise
+  // transposing read of lane (j, g): key 4g + j/4 (+16 hh) of the chunk, the
+  // 8 bytes at d = 16 nn + 4 (j % 4)
+  const int voff = g * 128 + (r >> 2) * 32 + (r & 3) * 8;
+  // tiles of this wave that some row selected, and per-lane row selection:
+  // bias 0 for a selected row, -inf otherwise
   float bias[kPfTiles];
-  bool active[kPfTiles];
+  int tiles = 0;
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
     const uint32_t tile_bits = ((1u << RT) - 1u) << ((wave * kPfTiles + i) * RT);
-    active[i] = (bmask & tile_bits) != 0u;
+    tiles |= (bmask & tile_bits) ? (1 << i) : 0;
     const bool sel = w.lrow[i] >= 0 && ((bmask >> w.lrow[i]) & 1u);
     bias[i] = sel ? 0.f : -INFINITY;
   }
   const int kpos_blk = blk * kBlockTokens;
+  const u32x4 ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 x 8
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_w);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    // operands of this 32-key chunk, shared by the wave's active tiles
     bf16x8 kop[2][KK];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        kop[tt][kk] = *reinterpret_cast<const bf16x8*>(kb + (c * 32 + 16 * tt) * 256 + koff[kk]);
-    // V^T operand of output tile nn: lane (r, g) reads d = 16 nn + r, keys
-    // tau(8g .. 8g+7) of the chunk: one 16-byte V^T cell.
     bf16x8 vop[NN];
+    if (tiles) {
+      // operands of this 32-key chunk, shared by the wave's active tiles
 #pragma unroll
-    for (int nn = 0; nn < NN; ++nn)
-      vop[nn] = *reinterpret_cast<const bf16x8*>(vtb + c * 8192 + vt_cell(16 * nn + r, g));
-    const int kbase = kpos_blk + c * 32 + 4 * g;
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int i = 0; i < kPfTiles; ++i) {
-      if (!active[i]) continue;
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < KK; ++kk)
+          kop[tt][kk] = *reinterpret_cast<const bf16x8*>(kb + (c * 32 + 16 * tt) * 256 + koff[kk]);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s0 = mfma16(kop[0][kk], w.qop[i][kk], s0);
-        s1 = mfma16(kop[1][kk], w.qop[i][kk], s1);
+      for (int nn = 0; nn < NN; ++nn) {
+        const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4i16 __attribute__((address_space(3)))*)((const lds_u8*)vb + nn * 4096 + c * 1024 + voff));
+        const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4i16 __attribute__((address_space(3)))*)((const lds_u8*)vb + nn * 4096 + c * 1024 + 512 + voff));
+        const u32x2 l0 = __builtin_bit_cast(u32x2, h0), l1 = __builtin_bit_cast(u32x2, h1);
+        vop[nn] = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
       }
-      float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      if (causal) {
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const int kp = kbase + (ii & 3) + ((ii >> 2) << 4);
-          sv[ii] = kp <= w.lpos[i] ? sv[ii] : -INFINITY;
-        }
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int ii = 1; ii < 8; ++ii) mx = fmaxf(mx, sv[ii]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxs = fmaf(mx, sl2, bias[i]);            // chunk max, scaled (log2 units)
-      if (__ballot(mxs > w.m[i] + kLazy)) {                // rare after the first chunks
-        const float m_new = fmaxf(w.m[i], mxs);
-        const float alpha = exp2_fast(w.m[i] - (m_new == -INFINITY ? 0.f : m_new));
-        w.l[i] *= alpha;
-#pragma unroll
-        for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = w.acc[i][nn] * alpha;
-        w.m[i] = m_new;
-      }
-      const float off = bias[i] - (w.m[i] == -INFINITY ? 0.f : w.m[i]);
-      float p[8], ps = 0.f;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        p[ii] = exp2_fast(fmaf(sv[ii], sl2, off));
-        ps += p[ii];
-      }
-      w.l[i] += ps;
-      const u32x4 pw = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = mfma16(vop[nn], pop, w.acc[i][nn]);
+    }
+    if (nx.valid) pf_issue_part(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len, c);
+    if (tiles) {
+      const int kbase = kpos_blk + c * 32 + 4 * g;
+      if (tiles == 3) pf_chunk<3>(w, kop, vop, bias, ones, sl2, causal, kbase);
+      else if (tiles == 1) pf_chunk<1>(w, kop, vop, bias, ones, sl2, causal, kbase);
+      else pf_chunk<2>(w, kop, vop, bias, ones, sl2, causal, kbase);
     }
   }
 }
@@ -218,7 +260,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   // two K/V buffers as distinct LDS objects: the loop below is unrolled by two,
   // so the compiler knows the in-flight copies target the other buffer
   __shared__ __align__(16) uint8_t k0[kPfBlockBytes], k1[kPfBlockBytes];
-  __shared__ __align__(16) uint8_t vnat[kPfBlockBytes], vt[kPfBlockBytes];
+  __shared__ __align__(16) uint8_t v0[kPfBlockBytes], v1[kPfBlockBytes];
   __shared__ uint32_t s_mask[kPfMaxBlocks];
   __shared__ uint16_t s_list[kPfMaxBlocks];   // selected blocks, ascending
   __shared__ int32_t s_phys[kPfMaxBlocks];    // their physical block ids
@@ -327,7 +369,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
     w.lrow[i] = ok ? rr : -1;
     w.lpos[i] = pos_first + rr;
     w.m[i] = -INFINITY;
-    w.l[i] = 0.f;
+    w.lacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
                           (((int64_t)(row0 + (ok ? rr : 0)) * a.num_q_heads + kvh * G + (r % G)) * D) * 2;
 #pragma unroll
@@ -343,32 +385,34 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   __syncthreads();
   const int n_act = s_info[0];
 
-  if (n_act > 0) pf_issue_block((lds_u8*)k0, (lds_u8*)vnat, a, kvh, s_phys[0], s_list[0], seq_len);
+  if (n_act > 0) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part)
+      pf_issue_part((lds_u8*)k0, (lds_u8*)v0, a, kvh, s_phys[0], s_list[0], seq_len, part);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const uint32_t wave_bits = ((1u << (kPfTiles * RT)) - 1u) << (wave * kPfTiles * RT);
   const int own_first = pos_first / kBlockTokens;   // blocks before it are wholly in every row's past
   for (int it = 0; it < n_act; it += 2) {
-    // even step: K in k0; the next block's K goes to k1
+    // even step: block in (k0, v0); the next one goes to (k1, v1)
     {
-      pf_transpose_v(vnat, vt);
-      __syncthreads();
-      if (it + 1 < n_act) pf_issue_block((lds_u8*)k1, (lds_u8*)vnat, a, kvh, s_phys[it + 1], s_list[it + 1], seq_len);
       const int j = s_list[it];
-      const uint32_t bmask = s_mask[j];
-      if (bmask & wave_bits) pf_compute_block(w, k0, vt, bmask, j, wave, RT, sl2, j >= own_first);
+      const PfNext nx = {(lds_u8*)k1, (lds_u8*)v1, it + 1 < n_act ? s_phys[it + 1] : 0,
+                         it + 1 < n_act ? (int)s_list[it + 1] : 0, it + 1 < n_act};
+      const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
+      pf_compute_block(w, k0, v0, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
       __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
       __syncthreads();
     }
     if (it + 1 >= n_act) break;
-    // odd step: K in k1; the next block's K goes to k0
+    // odd step: block in (k1, v1); the next one goes to (k0, v0)
     {
-      pf_transpose_v(vnat, vt);
-      __syncthreads();
-      if (it + 2 < n_act) pf_issue_block((lds_u8*)k0, (lds_u8*)vnat, a, kvh, s_phys[it + 2], s_list[it + 2], seq_len);
       const int j = s_list[it + 1];
-      const uint32_t bmask = s_mask[j];
-      if (bmask & wave_bits) pf_compute_block(w, k1, vt, bmask, j, wave, RT, sl2, j >= own_first);
+      const PfNext nx = {(lds_u8*)k0, (lds_u8*)v0, it + 2 < n_act ? s_phys[it + 2] : 0,
+                         it + 2 < n_act ? (int)s_list[it + 2] : 0, it + 2 < n_act};
+      const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
+      pf_compute_block(w, k1, v1, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -378,9 +422,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   const float vscale = a.v_scale ? *a.v_scale : 1.f;
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
-    float L = w.l[i];
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
+    const float L = w.lacc[i][0];      // every entry holds the head's full sum
     if (w.lrow[i] < 0) continue;
     const float inv = L > 0.f ? vscale / L : 0.f;
     uint8_t* orow = reinterpret_cast<uint8_t*>(a.out) +
