@@ -87,46 +87,46 @@ __device__ __forceinline__ T load_or_zero(bool ok, const void* p) {
   return ok ? *reinterpret_cast<const T*>(p) : z;
 }
 
-// Load one chunk: c = chunk index within the row's compacted context.
-template <int FMT, int D>
-__device__ __forceinline__ void load_chunk(ChunkRaw<FMT, D>& raw, const AttendArgs& a, const int* slot_list,
-                                           int c, int ctx, int kvh, int lane) {
-  constexpr int KK = D / 32, NN = D / 16;
-  const int r = lane & 15, g = lane >> 4;
+// Where chunk c (32 tokens of the row's compacted context) lives.
+struct ChunkAddr {
+  int64_t pg0;      // K page of the chunk's first 16 tokens (the next page holds the rest)
+  int64_t vpg0;     // V page (bf16 / fp8: pg0 + the V page offset)
+  bool ok;          // the block's pages lie inside the cache
+};
+
+template <int FMT>
+__device__ __forceinline__ ChunkAddr chunk_addr(const AttendArgs& a, const int* slot_list, int c) {
   const int phys = __builtin_amdgcn_readfirstlane(slot_list[c >> 2]);
-  const int64_t pg0 = (int64_t)phys * a.block_page_stride + 2 * (c & 3);
-  const int64_t vpg0 = pg0 + a.v_page_offset;
-  const bool chunk_ok = phys >= 0 && pg0 + 1 < a.num_pages && (FMT == kFmtNvfp4 || vpg0 + 1 < a.num_pages);
+  ChunkAddr ca;
+  ca.pg0 = (int64_t)phys * a.block_page_stride + 2 * (c & 3);
+  ca.vpg0 = ca.pg0 + a.v_page_offset;
+  ca.ok = phys >= 0 && ca.pg0 + 1 < a.num_pages && (FMT == kFmtNvfp4 || ca.vpg0 + 1 < a.num_pages);
+  return ca;
+}
+
+// K half of chunk c (tokens past ctx, or of a block outside the cache, read as 0).
+template <int FMT, int D>
+__device__ __forceinline__ void load_k(ChunkRaw<FMT, D>& raw, const AttendArgs& a, const ChunkAddr& ca, int c,
+                                       int ctx, int kvh, int lane) {
+  constexpr int KK = D / 32;
+  const int r = lane & 15, g = lane >> 4;
   const int tok0 = c * 32;
   if constexpr (FMT == kFmtNvfp4) {
     constexpr int SLOT = 9 * D, CODE_ROW = D / 2, SCALE_ROW = D / 16;
-    const uint8_t* kslot = a.k_base + pg0 * a.page_stride + (int64_t)(2 * kvh) * SLOT;
+    const uint8_t* kslot = a.k_base + ca.pg0 * a.page_stride + (int64_t)(2 * kvh) * SLOT;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bool ok = chunk_ok && tok0 + 16 * t + r < ctx;
+      const bool ok = ca.ok && tok0 + 16 * t + r < ctx;
       const uint8_t* s = kslot + t * a.page_stride;
       raw.k[t] = load_or_zero<u32x4>(ok, s + r * CODE_ROW + 16 * g);
       raw.ks[t] = ok ? (uint32_t) * reinterpret_cast<const uint16_t*>(s + 16 * CODE_ROW + r * SCALE_ROW + 2 * g) : 0u;
     }
-    const uint8_t* vslot = kslot + SLOT;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-      const bool ok = chunk_ok && tok0 + t < ctx;
-      const uint8_t* s = vslot + (t >> 4) * a.page_stride;
-      const int tr = t & 15;
-      raw.v[i] = load_or_zero<uint32_t>(ok, s + tr * CODE_ROW + 4 * r);
-      raw.vs[i] = ok ? (uint32_t)s[16 * CODE_ROW + tr * SCALE_ROW + (r >> 1)] : 0u;
-    }
   } else {
-    constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1;
-    constexpr int ROW = D * ESZ;
-    const int64_t head_off = (int64_t)kvh * kPageTokens * ROW;
-    const uint8_t* kp = a.k_base + pg0 * a.page_stride + head_off;
-    const uint8_t* vp = a.v_base + vpg0 * a.page_stride + head_off;
+    constexpr int ROW = D * (FMT == kFmtBf16 ? 2 : 1);
+    const uint8_t* kp = a.k_base + ca.pg0 * a.page_stride + (int64_t)kvh * kPageTokens * ROW;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bool ok = chunk_ok && tok0 + 16 * t + r < ctx;
+      const bool ok = ca.ok && tok0 + 16 * t + r < ctx;
       const uint8_t* row = kp + t * a.page_stride + r * ROW;
       if constexpr (FMT == kFmtBf16) {
 #pragma unroll
@@ -136,10 +136,37 @@ __device__ __forceinline__ void load_chunk(ChunkRaw<FMT, D>& raw, const AttendAr
         for (int kp2 = 0; kp2 < KK / 2; ++kp2) raw.k[t][kp2] = load_or_zero<u32x4>(ok, row + kappa<FMT, D>(2 * kp2, g));
       }
     }
+  }
+}
+
+// V half of chunk c: lane (r, g) takes token rows tau(8g + i) (4g + i of the
+// first page for i < 4, 4g + i - 4 of the second), columns r * NN .. + NN.
+template <int FMT, int D>
+__device__ __forceinline__ void load_v(ChunkRaw<FMT, D>& raw, const AttendArgs& a, const ChunkAddr& ca, int c,
+                                       int ctx, int kvh, int lane) {
+  constexpr int NN = D / 16;
+  const int r = lane & 15, g = lane >> 4;
+  const int tok0 = c * 32;
+  if constexpr (FMT == kFmtNvfp4) {
+    constexpr int SLOT = 9 * D, CODE_ROW = D / 2, SCALE_ROW = D / 16;
+    const uint8_t* vslot = a.k_base + ca.pg0 * a.page_stride + (int64_t)(2 * kvh + 1) * SLOT;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-      const bool ok = chunk_ok && tok0 + t < ctx;
+      const bool ok = ca.ok && tok0 + t < ctx;
+      const uint8_t* s = vslot + (t >> 4) * a.page_stride;
+      const int tr = t & 15;
+      raw.v[i] = load_or_zero<uint32_t>(ok, s + tr * CODE_ROW + 4 * r);
+      raw.vs[i] = ok ? (uint32_t)s[16 * CODE_ROW + tr * SCALE_ROW + (r >> 1)] : 0u;
+    }
+  } else {
+    constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1;
+    constexpr int ROW = D * ESZ;
+    const uint8_t* vp = a.v_base + ca.vpg0 * a.page_stride + (int64_t)kvh * kPageTokens * ROW;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
+      const bool ok = ca.ok && tok0 + t < ctx;
       const uint8_t* row = vp + (t >> 4) * a.page_stride + (t & 15) * ROW + r * NN * ESZ;
       if constexpr (FMT == kFmtBf16) {
         if constexpr (NN / 2 == 4) {
@@ -215,14 +242,23 @@ template <int FMT, int D>
 struct WaveState {
   static constexpr int NN = D / 16;
   f32x4 acc[NN];
-  float m;   // running max (log2 domain), same on the 4 lanes of a head
-  float l;   // this lane's share of the softmax denominator
+  f32x4 lacc;  // softmax denominator: P times an all-ones operand (every entry = the head's sum)
+  float m;     // reference max (log2 units), the same on the 4 lanes of a head
 };
 
+// The online softmax rescales only when some lane's chunk max exceeds the
+// reference by more than kLazy (log2 units): probabilities stay below 2^kLazy
+// and the common case needs neither a cross-lane max nor a rescale.
+constexpr float kLazyMax = 8.f;
+
+// One 32-token chunk of one wave.  The next chunk's K is loaded as soon as
+// this chunk's QK^T products have consumed K, and its V once the V operands
+// are built, so one set of staging registers suffices.
 template <int FMT, int D>
-__device__ __forceinline__ void process_chunk(WaveState<FMT, D>& st, const ChunkRaw<FMT, D>& raw,
+__device__ __forceinline__ void process_chunk(WaveState<FMT, D>& st, ChunkRaw<FMT, D>& raw,
                                               const typename OpType<FMT>::type* qop, float sl2, int c, int ctx,
-                                              bool chunk_ok, int lane) {
+                                              bool chunk_ok, int lane, const AttendArgs& a, const int* slot_list,
+                                              int c_next, bool more, int kvh) {
   constexpr int KK = D / 32, NN = D / 16;
   typedef typename OpType<FMT>::type OT;
   const int g = lane >> 4;
@@ -232,41 +268,51 @@ __device__ __forceinline__ void process_chunk(WaveState<FMT, D>& st, const Chunk
     s0 = mfma16(k_operand<FMT, D>(raw, 0, kk), qop[kk], s0);
     s1 = mfma16(k_operand<FMT, D>(raw, 1, kk), qop[kk], s1);
   }
+  ChunkAddr nca;
+  if (more) {
+    nca = chunk_addr<FMT>(a, slot_list, c_next);
+    load_k<FMT, D>(raw, a, nca, c_next, ctx, kvh, lane);
+  }
   // online softmax over this chunk's 32 tokens
   const int tok0 = c * 32 + 4 * g;
   float sc[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sc[i] = (chunk_ok && tok0 + i < ctx) ? s0[i] * sl2 : -INFINITY;
-    sc[4 + i] = (chunk_ok && tok0 + 16 + i < ctx) ? s1[i] * sl2 : -INFINITY;
+    sc[i] = (chunk_ok && tok0 + i < ctx) ? s0[i] : -INFINITY;
+    sc[4 + i] = (chunk_ok && tok0 + 16 + i < ctx) ? s1[i] : -INFINITY;
   }
   float mx = sc[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = exp2_fast(st.m - m_use);
-  float p[8], psum = 0.f;
+  const float mxs = mx * sl2;
+  if (__ballot(mxs > st.m + kLazyMax)) {   // rare after the first chunk
+    float mh = fmaxf(mxs, __shfl_xor(mxs, 16));
+    mh = fmaxf(mh, __shfl_xor(mh, 32));
+    const float m_new = fmaxf(st.m, mh);
+    const float alpha = exp2_fast(st.m - (m_new == -INFINITY ? 0.f : m_new));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = exp2_fast(sc[i] - m_use);
-    psum += p[i];
+    for (int nn = 0; nn < NN; ++nn) st.acc[nn] = st.acc[nn] * alpha;
+    st.lacc = st.lacc * alpha;
+    st.m = m_new;
   }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-  u32x4 pw;
+  const float off = -(st.m == -INFINITY ? 0.f : st.m);
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(sc[i], sl2, off));
+  u32x4 pw, onesw;
   if constexpr (FMT == kFmtNvfp4) {
     pw = u32x4{pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]), pack_f16(p[6], p[7])};
+    onesw = u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
   } else {
     pw = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+    onesw = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   }
   const OT pop = __builtin_bit_cast(OT, pw);
-  // V rows -> transposed operands, then O^T += V^T P^T
+  // V rows -> transposed operands (V^T rows d = r * NN + nn, keys tau(8g + i))
   uint32_t rows[8][NN / 2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v_row<FMT, D>(raw, i, rows[i]);
+  OT vop[NN];
 #pragma unroll
   for (int nn = 0; nn < NN; ++nn) {
     u32x4 vw;
@@ -275,9 +321,12 @@ __device__ __forceinline__ void process_chunk(WaveState<FMT, D>& st, const Chunk
       const uint32_t a0 = rows[2 * pr][nn >> 1], a1 = rows[2 * pr + 1][nn >> 1];
       vw[pr] = (nn & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
     }
-    st.acc[nn] = st.acc[nn] * alpha;
-    st.acc[nn] = mfma16(__builtin_bit_cast(OT, vw), pop, st.acc[nn]);
+    vop[nn] = __builtin_bit_cast(OT, vw);
   }
+  if (more) load_v<FMT, D>(raw, a, nca, c_next, ctx, kvh, lane);
+#pragma unroll
+  for (int nn = 0; nn < NN; ++nn) st.acc[nn] = mfma16(vop[nn], pop, st.acc[nn]);
+  st.lacc = mfma16(__builtin_bit_cast(OT, onesw), pop, st.lacc);
 }
 
 // Shared memory of one workgroup.
@@ -342,32 +391,23 @@ __global__ __launch_bounds__(256) void attend_rows_kernel(const AttendArgs a) {
   WaveState<FMT, D> st;
 #pragma unroll
   for (int nn = 0; nn < NN; ++nn) st.acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.lacc = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
-  st.l = 0.f;
 
-  auto ok_of = [&](int c) {
-    const int phys = sm.slot_list[c >> 2];
-    const int64_t pg0 = (int64_t)phys * a.block_page_stride + 2 * (c & 3);
-    return phys >= 0 && pg0 + 1 < a.num_pages &&
-           (FMT == kFmtNvfp4 || pg0 + a.v_page_offset + 1 < a.num_pages);
-  };
-  ChunkRaw<FMT, D> bufA, bufB;
+  ChunkRaw<FMT, D> raw;
   int c = c0 + wave;
-  if (c < c1) load_chunk<FMT, D>(bufA, a, sm.slot_list, c, ctx, kvh, lane);
-  while (c < c1) {
-    if (c + 4 < c1) load_chunk<FMT, D>(bufB, a, sm.slot_list, c + 4, ctx, kvh, lane);
-    process_chunk<FMT, D>(st, bufA, qop, sl2, c, ctx, ok_of(c), lane);
-    c += 4;
-    if (c >= c1) break;
-    if (c + 4 < c1) load_chunk<FMT, D>(bufA, a, sm.slot_list, c + 4, ctx, kvh, lane);
-    process_chunk<FMT, D>(st, bufB, qop, sl2, c, ctx, ok_of(c), lane);
-    c += 4;
+  if (c < c1) {
+    const ChunkAddr ca = chunk_addr<FMT>(a, sm.slot_list, c);
+    load_k<FMT, D>(raw, a, ca, c, ctx, kvh, lane);
+    load_v<FMT, D>(raw, a, ca, c, ctx, kvh, lane);
+  }
+  for (; c < c1; c += 4) {
+    const bool ok = chunk_addr<FMT>(a, sm.slot_list, c).ok;
+    process_chunk<FMT, D>(st, raw, qop, sl2, c, ctx, ok, lane, a, sm.slot_list, c + 4, c + 4 < c1, kvh);
   }
 
   // merge the four waves through LDS
-  float lsum = st.l;
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  const float lsum = st.lacc[0];
   if (r < G) {
     if (g == 0) {
       sm.m[wave][r] = st.m;
