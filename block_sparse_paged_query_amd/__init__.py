@@ -235,6 +235,9 @@ def msa_sparse_decode(q, kv: KVCache, topk, block_table, seq_lens, softmax_scale
     if d != kv.head_dim:
         raise ValueError(f"q head_dim {d} != cache head_dim {kv.head_dim}")
     num_reqs = seq_lens.shape[0]
+    if rows != num_reqs * decode_query_len:
+        raise ValueError(f"q has {rows} rows; {num_reqs} requests x decode_query_len {decode_query_len} "
+                         f"= {num_reqs * decode_query_len}")
     if workspace is None:
         nbytes = msa_decode_workspace_size(rows, hq, d, topk.shape[1])
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)

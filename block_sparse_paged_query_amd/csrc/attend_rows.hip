@@ -16,10 +16,15 @@
 // the causal tail) in LDS.  The row's context [0, ctx) is cut into 32-token
 // chunks (two 16-token pages of one 128-token block); a split owns a
 // contiguous range of chunks and its four waves take every fourth chunk.
-// Each wave keeps its own online-softmax state, loads the next chunk while it
-// computes the current one, and the four states are merged through LDS at
-// the end.  With one split the workgroup writes the bf16 output directly;
-// otherwise it writes an fp32 partial (o, m, l) and attend_merge combines.
+// Each wave keeps its own online-softmax state and several chunks' loads in
+// flight; the four states are merged through LDS at the end.  With one split
+// the workgroup writes the bf16 output directly; otherwise it writes an fp32
+// partial (o, m, l) and attend_merge combines.
+//
+// Loads go through raw-buffer descriptors built per page in scalar
+// registers, sized to the page's tokens inside the context: the hardware
+// returns 0 for the rest, so neither the tail nor a bad block id needs a
+// branch or a select per load, and lane addresses are loop constants.
 //
 // Per chunk, one wave computes S^T = K Q^T (tokens x heads) and
 // O^T += V^T P^T (head_dim x heads) on 16x16x32 matrix cores, the GQA group
@@ -51,6 +56,11 @@ __device__ __forceinline__ constexpr int kappa(int kk, int g) {
     return (D / 4) * g + 8 * kk;                   // 16 B of e2m1 at 16g (D = 128)
   }
 }
+
+// Chunks a wave keeps in flight: enough bytes to cover the memory latency
+// within the register budget of two waves per SIMD.
+template <int FMT>
+constexpr int kStages = FMT == kFmtBf16 ? 2 : (FMT == kFmtFp8 ? 3 : 4);
 
 template <int FMT, int D>
 struct ChunkRaw;
@@ -87,101 +97,153 @@ __device__ __forceinline__ T load_or_zero(bool ok, const void* p) {
   return ok ? *reinterpret_cast<const T*>(p) : z;
 }
 
-// Where chunk c (32 tokens of the row's compacted context) lives.
-struct ChunkAddr {
-  int64_t pg0;      // K page of the chunk's first 16 tokens (the next page holds the rest)
-  int64_t vpg0;     // V page (bf16 / fp8: pg0 + the V page offset)
-  bool ok;          // the block's pages lie inside the cache
+// Raw-buffer descriptors (gfx9 layout, unit stride, no swizzle): a load at
+// or past num_records bytes returns 0 and touches no memory, which masks the
+// tokens past the context and blocks outside the cache without branches.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr int kRawBufferWord3 = 0x00020000;   // 32-bit data format
+
+__device__ __forceinline__ BufRsrc make_rsrc(const uint8_t* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, bytes, kRawBufferWord3);
+}
+// AUX is the load's cache policy: 0 normal, kStreamLoads non-temporal
+// (lines are not kept for reuse).
+constexpr int kStreamLoads = 2;
+
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_load16(BufRsrc r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ u32x2 buf_load8(BufRsrc r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ uint32_t buf_load4(BufRsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ uint32_t buf_load2(BufRsrc r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ uint32_t buf_load1(BufRsrc r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, AUX);
+}
+
+// Byte offsets of one lane's loads inside a page tile (bf16 / fp8: the
+// [16][D] tile of one kv head) or inside an NVFP4 slot's code / scale rows.
+// K: token r of each page; V: tokens 4g .. 4g+3 of each page (tau order),
+// columns r*NN .. r*NN + NN.
+struct LaneOffsets {
+  uint32_t k, v, ks, vs;
 };
 
-template <int FMT>
-__device__ __forceinline__ ChunkAddr chunk_addr(const AttendArgs& a, const int* slot_list, int c) {
-  const int phys = __builtin_amdgcn_readfirstlane(slot_list[c >> 2]);
-  ChunkAddr ca;
-  ca.pg0 = (int64_t)phys * a.block_page_stride + 2 * (c & 3);
-  ca.vpg0 = ca.pg0 + a.v_page_offset;
-  ca.ok = phys >= 0 && ca.pg0 + 1 < a.num_pages && (FMT == kFmtNvfp4 || ca.vpg0 + 1 < a.num_pages);
-  return ca;
+template <int FMT, int D>
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  LaneOffsets o;
+  if constexpr (FMT == kFmtNvfp4) {
+    o.k = r * (D / 2) + 16 * g;           // 32 codes: d in [32g, 32g + 32)
+    o.ks = r * (D / 16) + 2 * g;          // scales of groups 2g and 2g + 1
+    o.v = 4 * g * (D / 2) + 4 * r;        // 8 codes: d in [8r, 8r + 8)
+    o.vs = 4 * g * (D / 16) + (r >> 1);   // the scale of group r / 2
+  } else {
+    constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1, ROW = D * ESZ, NN = D / 16;
+    o.k = r * ROW + 16 * g;
+    o.v = 4 * g * ROW + r * NN * ESZ;
+    o.ks = o.vs = 0;
+  }
+  return o;
 }
 
-// K half of chunk c (tokens past ctx, or of a block outside the cache, read as 0).
+// Where chunk c (32 tokens of the row's compacted context: pages 2(c%4) and
+// 2(c%4)+1 of block slot c/4) lives.  Wave-uniform.
+struct ChunkLoc {
+  const uint8_t* k[2];   // K page tiles (NVFP4: K slots) of the two pages
+  const uint8_t* v[2];   // V page tiles (NVFP4: V slots)
+  int valid[2];          // tokens of each page inside the context; 0 past c_end or outside the cache
+  bool ok;               // the block's pages lie inside the cache
+};
+
 template <int FMT, int D>
-__device__ __forceinline__ void load_k(ChunkRaw<FMT, D>& raw, const AttendArgs& a, const ChunkAddr& ca, int c,
-                                       int ctx, int kvh, int lane) {
-  constexpr int KK = D / 32;
-  const int r = lane & 15, g = lane >> 4;
-  const int tok0 = c * 32;
-  if constexpr (FMT == kFmtNvfp4) {
-    constexpr int SLOT = 9 * D, CODE_ROW = D / 2, SCALE_ROW = D / 16;
-    const uint8_t* kslot = a.k_base + ca.pg0 * a.page_stride + (int64_t)(2 * kvh) * SLOT;
+__device__ __forceinline__ ChunkLoc chunk_loc(const AttendArgs& a, const int* slot_list, int c, int c_end, int ctx,
+                                              int kvh) {
+  ChunkLoc L;
+  const bool in = c < c_end;
+  const int phys = __builtin_amdgcn_readfirstlane(slot_list[in ? (c >> 2) : 0]);
+  const int64_t pg0 = (int64_t)phys * a.block_page_stride + 2 * (c & 3);
+  // (the 64-bit compares run on the vector unit: take the verdict back to a scalar)
+  L.ok = __builtin_amdgcn_readfirstlane(
+      (int)(phys >= 0 && pg0 + 1 < a.num_pages && (FMT == kFmtNvfp4 || pg0 + a.v_page_offset + 1 < a.num_pages)));
+  const int rem = ctx - c * 32;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bool ok = ca.ok && tok0 + 16 * t + r < ctx;
-      const uint8_t* s = kslot + t * a.page_stride;
-      raw.k[t] = load_or_zero<u32x4>(ok, s + r * CODE_ROW + 16 * g);
-      raw.ks[t] = ok ? (uint32_t) * reinterpret_cast<const uint16_t*>(s + 16 * CODE_ROW + r * SCALE_ROW + 2 * g) : 0u;
-    }
-  } else {
-    constexpr int ROW = D * (FMT == kFmtBf16 ? 2 : 1);
-    const uint8_t* kp = a.k_base + ca.pg0 * a.page_stride + (int64_t)kvh * kPageTokens * ROW;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bool ok = ca.ok && tok0 + 16 * t + r < ctx;
-      const uint8_t* row = kp + t * a.page_stride + r * ROW;
-      if constexpr (FMT == kFmtBf16) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) raw.k[t][kk] = load_or_zero<u32x4>(ok, row + 2 * kappa<FMT, D>(kk, g));
-      } else {
-#pragma unroll
-        for (int kp2 = 0; kp2 < KK / 2; ++kp2) raw.k[t][kp2] = load_or_zero<u32x4>(ok, row + kappa<FMT, D>(2 * kp2, g));
-      }
+  for (int t = 0; t < 2; ++t) {
+    L.valid[t] = __builtin_amdgcn_readfirstlane((in && L.ok) ? min(max(rem - 16 * t, 0), kPageTokens) : 0);
+    if constexpr (FMT == kFmtNvfp4) {
+      constexpr int SLOT = 9 * D;
+      L.k[t] = a.k_base + (pg0 + t) * a.page_stride + (int64_t)(2 * kvh) * SLOT;
+      L.v[t] = L.k[t] + SLOT;
+    } else {
+      constexpr int ROW = D * (FMT == kFmtBf16 ? 2 : 1);
+      L.k[t] = a.k_base + (pg0 + t) * a.page_stride + (int64_t)kvh * kPageTokens * ROW;
+      L.v[t] = a.v_base + (pg0 + a.v_page_offset + t) * a.page_stride + (int64_t)kvh * kPageTokens * ROW;
     }
   }
+  return L;
 }
 
-// V half of chunk c: lane (r, g) takes token rows tau(8g + i) (4g + i of the
-// first page for i < 4, 4g + i - 4 of the second), columns r * NN .. + NN.
-template <int FMT, int D>
-__device__ __forceinline__ void load_v(ChunkRaw<FMT, D>& raw, const AttendArgs& a, const ChunkAddr& ca, int c,
-                                       int ctx, int kvh, int lane) {
-  constexpr int NN = D / 16;
-  const int r = lane & 15, g = lane >> 4;
-  const int tok0 = c * 32;
+// Issue every load of one chunk (tokens past the context read as 0).
+template <int FMT, int D, int AUX>
+__device__ __forceinline__ void issue_loads(ChunkRaw<FMT, D>& raw, const ChunkLoc& L, const LaneOffsets& o) {
+  constexpr int KK = D / 32, NN = D / 16;
   if constexpr (FMT == kFmtNvfp4) {
-    constexpr int SLOT = 9 * D, CODE_ROW = D / 2, SCALE_ROW = D / 16;
-    const uint8_t* vslot = a.k_base + ca.pg0 * a.page_stride + (int64_t)(2 * kvh + 1) * SLOT;
+    constexpr int CODE = D / 2, SCALE = D / 16, SREG = kPageTokens * CODE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-      const bool ok = ca.ok && tok0 + t < ctx;
-      const uint8_t* s = vslot + (t >> 4) * a.page_stride;
-      const int tr = t & 15;
-      raw.v[i] = load_or_zero<uint32_t>(ok, s + tr * CODE_ROW + 4 * r);
-      raw.vs[i] = ok ? (uint32_t)s[16 * CODE_ROW + tr * SCALE_ROW + (r >> 1)] : 0u;
+    for (int t = 0; t < 2; ++t) {
+      const BufRsrc kc = make_rsrc(L.k[t], L.valid[t] * CODE);
+      const BufRsrc ksr = make_rsrc(L.k[t] + SREG, L.valid[t] * SCALE);
+      raw.k[t] = buf_load16<AUX>(kc, o.k);
+      raw.ks[t] = buf_load2<AUX>(ksr, o.ks);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const BufRsrc vc = make_rsrc(L.v[t], L.valid[t] * CODE);
+      const BufRsrc vsr = make_rsrc(L.v[t] + SREG, L.valid[t] * SCALE);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        raw.v[4 * t + i] = buf_load4<AUX>(vc, o.v + i * CODE);
+        raw.vs[4 * t + i] = buf_load1<AUX>(vsr, o.vs + i * SCALE);
+      }
     }
   } else {
-    constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1;
-    constexpr int ROW = D * ESZ;
-    const uint8_t* vp = a.v_base + ca.vpg0 * a.page_stride + (int64_t)kvh * kPageTokens * ROW;
+    constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1, ROW = D * ESZ;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-      const bool ok = ca.ok && tok0 + t < ctx;
-      const uint8_t* row = vp + (t >> 4) * a.page_stride + (t & 15) * ROW + r * NN * ESZ;
+    for (int t = 0; t < 2; ++t) {
+      const BufRsrc kr = make_rsrc(L.k[t], L.valid[t] * ROW);
       if constexpr (FMT == kFmtBf16) {
-        if constexpr (NN / 2 == 4) {
-          const u32x4 x = load_or_zero<u32x4>(ok, row);
-          raw.v[i][0] = x[0]; raw.v[i][1] = x[1]; raw.v[i][2] = x[2]; raw.v[i][3] = x[3];
-        } else {
-          const u32x2 x = load_or_zero<u32x2>(ok, row);
-          raw.v[i][0] = x[0]; raw.v[i][1] = x[1];
-        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) raw.k[t][kk] = buf_load16<AUX>(kr, o.k + 64 * kk);
       } else {
-        if constexpr (NN / 4 == 2) {
-          const u32x2 x = load_or_zero<u32x2>(ok, row);
-          raw.v[i][0] = x[0]; raw.v[i][1] = x[1];
+#pragma unroll
+        for (int kp = 0; kp < KK / 2; ++kp) raw.k[t][kp] = buf_load16<AUX>(kr, o.k + 64 * kp);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const BufRsrc vr = make_rsrc(L.v[t], L.valid[t] * ROW);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t* dst = raw.v[4 * t + i];
+        constexpr int W = NN * ESZ / 4;   // dwords of one lane's row piece
+        if constexpr (W == 4) {
+          const u32x4 x = buf_load16<AUX>(vr, o.v + i * ROW);
+          dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
+        } else if constexpr (W == 2) {
+          const u32x2 x = buf_load8<AUX>(vr, o.v + i * ROW);
+          dst[0] = x[0]; dst[1] = x[1];
         } else {
-          raw.v[i][0] = load_or_zero<uint32_t>(ok, row);
+          dst[0] = buf_load4<AUX>(vr, o.v + i * ROW);
         }
       }
     }
@@ -214,27 +276,49 @@ __device__ __forceinline__ typename OpType<FMT>::type k_operand(const ChunkRaw<F
   }
 }
 
-// Decode V row i into NN half-precision values (packed pairs).
+// V^T operands: vop[nn] holds, for lane (r, g), column d = r*NN + nn of the
+// token rows tau(8g + 0 .. 7), as pairs (row 2p, row 2p+1).  The pairs are
+// formed on the raw codes where that is cheaper than on converted values:
+// a byte permute for fp8, a nibble merge for NVFP4 (one e2m1 byte then
+// converts straight into a (row 2p, row 2p+1) pair).
 template <int FMT, int D>
-__device__ __forceinline__ void v_row(const ChunkRaw<FMT, D>& raw, int i, uint32_t out[D / 32]) {
+__device__ __forceinline__ void v_operands(const ChunkRaw<FMT, D>& raw, u32x4 vop[D / 16]) {
   constexpr int NN = D / 16;
-  if constexpr (FMT == kFmtBf16) {
 #pragma unroll
-    for (int w = 0; w < NN / 2; ++w) out[w] = raw.v[i][w];
-  } else if constexpr (FMT == kFmtFp8) {
+  for (int p = 0; p < 4; ++p) {
+    if constexpr (FMT == kFmtBf16) {
 #pragma unroll
-    for (int w = 0; w < NN / 4; ++w) {
-      out[2 * w] = fp8x2_to_bf16x2<false>(raw.v[i][w]);
-      out[2 * w + 1] = fp8x2_to_bf16x2<true>(raw.v[i][w]);
+      for (int nn = 0; nn < NN; ++nn) {
+        const uint32_t a0 = raw.v[2 * p][nn >> 1], a1 = raw.v[2 * p + 1][nn >> 1];
+        vop[nn][p] = (nn & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
+      }
+    } else if constexpr (FMT == kFmtFp8) {
+#pragma unroll
+      for (int w = 0; w < NN / 4; ++w) {
+        const uint32_t a = raw.v[2 * p][w], b = raw.v[2 * p + 1][w];
+        // (a0, b0, a1, b1) and (a2, b2, a3, b3)
+        const uint32_t lo = (a & 0xffu) | ((b & 0xffu) << 8) | ((a & 0xff00u) << 8) | ((b & 0xff00u) << 16);
+        const uint32_t hi = ((a >> 16) & 0xffu) | ((b >> 8) & 0xff00u) | ((a >> 8) & 0xff0000u) | (b & 0xff000000u);
+        vop[4 * w + 0][p] = fp8x2_to_bf16x2<false>(lo);
+        vop[4 * w + 1][p] = fp8x2_to_bf16x2<true>(lo);
+        vop[4 * w + 2][p] = fp8x2_to_bf16x2<false>(hi);
+        vop[4 * w + 3][p] = fp8x2_to_bf16x2<true>(hi);
+      }
+    } else {
+      const uint32_t a = raw.v[2 * p], b = raw.v[2 * p + 1];
+      const f16x2 s = fp8x2_to_f16x2<false>(raw.vs[2 * p] | (raw.vs[2 * p + 1] << 8));   // (scale a, scale b)
+      // byte j of x: element 2j of a (low nibble) and of b (high nibble); y: element 2j + 1
+      const uint32_t x = (a & 0x0f0f0f0fu) | ((b << 4) & 0xf0f0f0f0u);
+      const uint32_t y = ((a >> 4) & 0x0f0f0f0fu) | (b & 0xf0f0f0f0u);
+      vop[0][p] = f16x2_bits(fp4x2_to_f16x2<0>(x) * s);
+      vop[2][p] = f16x2_bits(fp4x2_to_f16x2<1>(x) * s);
+      vop[4][p] = f16x2_bits(fp4x2_to_f16x2<2>(x) * s);
+      vop[6][p] = f16x2_bits(fp4x2_to_f16x2<3>(x) * s);
+      vop[1][p] = f16x2_bits(fp4x2_to_f16x2<0>(y) * s);
+      vop[3][p] = f16x2_bits(fp4x2_to_f16x2<1>(y) * s);
+      vop[5][p] = f16x2_bits(fp4x2_to_f16x2<2>(y) * s);
+      vop[7][p] = f16x2_bits(fp4x2_to_f16x2<3>(y) * s);
     }
-  } else {
-    const f16x2 sc = fp8x2_to_f16x2<false>(raw.vs[i]);
-    const f16x2 s = {sc[0], sc[0]};
-    const uint32_t w = raw.v[i];
-    out[0] = f16x2_bits(fp4x2_to_f16x2<0>(w) * s);
-    out[1] = f16x2_bits(fp4x2_to_f16x2<1>(w) * s);
-    out[2] = f16x2_bits(fp4x2_to_f16x2<2>(w) * s);
-    out[3] = f16x2_bits(fp4x2_to_f16x2<3>(w) * s);
   }
 }
 
@@ -251,35 +335,33 @@ struct WaveState {
 // and the common case needs neither a cross-lane max nor a rescale.
 constexpr float kLazyMax = 8.f;
 
-// One 32-token chunk of one wave.  The next chunk's K is loaded as soon as
-// this chunk's QK^T products have consumed K, and its V once the V operands
-// are built, so one set of staging registers suffices.
+// One 32-token chunk of one wave, from registers already loaded.  Scores of
+// tokens at or past `lim` are masked when `masked` (the context's last chunk,
+// or a block outside the cache, for which lim is 0).
 template <int FMT, int D>
-__device__ __forceinline__ void process_chunk(WaveState<FMT, D>& st, ChunkRaw<FMT, D>& raw,
-                                              const typename OpType<FMT>::type* qop, float sl2, int c, int ctx,
-                                              bool chunk_ok, int lane, const AttendArgs& a, const int* slot_list,
-                                              int c_next, bool more, int kvh) {
+__device__ __forceinline__ void compute_chunk(WaveState<FMT, D>& st, const ChunkRaw<FMT, D>& raw,
+                                              const typename OpType<FMT>::type* qop, float sl2, bool masked,
+                                              int tok0, int lim) {
   constexpr int KK = D / 32, NN = D / 16;
   typedef typename OpType<FMT>::type OT;
-  const int g = lane >> 4;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     s0 = mfma16(k_operand<FMT, D>(raw, 0, kk), qop[kk], s0);
     s1 = mfma16(k_operand<FMT, D>(raw, 1, kk), qop[kk], s1);
   }
-  ChunkAddr nca;
-  if (more) {
-    nca = chunk_addr<FMT>(a, slot_list, c_next);
-    load_k<FMT, D>(raw, a, nca, c_next, ctx, kvh, lane);
-  }
-  // online softmax over this chunk's 32 tokens
-  const int tok0 = c * 32 + 4 * g;
   float sc[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sc[i] = (chunk_ok && tok0 + i < ctx) ? s0[i] : -INFINITY;
-    sc[4 + i] = (chunk_ok && tok0 + 16 + i < ctx) ? s1[i] : -INFINITY;
+    sc[i] = s0[i];
+    sc[4 + i] = s1[i];
+  }
+  if (masked) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = tok0 + i < lim ? sc[i] : -INFINITY;
+      sc[4 + i] = tok0 + 16 + i < lim ? sc[4 + i] : -INFINITY;
+    }
   }
   float mx = sc[0];
 #pragma unroll
@@ -308,24 +390,10 @@ __device__ __forceinline__ void process_chunk(WaveState<FMT, D>& st, ChunkRaw<FM
     onesw = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   }
   const OT pop = __builtin_bit_cast(OT, pw);
-  // V rows -> transposed operands (V^T rows d = r * NN + nn, keys tau(8g + i))
-  uint32_t rows[8][NN / 2];
+  u32x4 vop[NN];
+  v_operands<FMT, D>(raw, vop);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v_row<FMT, D>(raw, i, rows[i]);
-  OT vop[NN];
-#pragma unroll
-  for (int nn = 0; nn < NN; ++nn) {
-    u32x4 vw;
-#pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      const uint32_t a0 = rows[2 * pr][nn >> 1], a1 = rows[2 * pr + 1][nn >> 1];
-      vw[pr] = (nn & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
-    }
-    vop[nn] = __builtin_bit_cast(OT, vw);
-  }
-  if (more) load_v<FMT, D>(raw, a, nca, c_next, ctx, kvh, lane);
-#pragma unroll
-  for (int nn = 0; nn < NN; ++nn) st.acc[nn] = mfma16(vop[nn], pop, st.acc[nn]);
+  for (int nn = 0; nn < NN; ++nn) st.acc[nn] = mfma16(__builtin_bit_cast(OT, vop[nn]), pop, st.acc[nn]);
   st.lacc = mfma16(__builtin_bit_cast(OT, onesw), pop, st.lacc);
 }
 
@@ -339,12 +407,12 @@ struct AttendSmem {
   float o[4][16][D];
 };
 
-template <int FMT, int D, int MODE>
-__global__ __launch_bounds__(256) void attend_rows_kernel(const AttendArgs a) {
-  constexpr int KK = D / 32, NN = D / 16;
+template <int FMT, int D, int MODE, int AUX>
+__global__ __launch_bounds__(256, 2) void attend_rows_kernel(const AttendArgs a) {
+  constexpr int KK = D / 32, NN = D / 16, NB = kStages<FMT>;
   typedef typename OpType<FMT>::type OT;
   __shared__ AttendSmem<D> sm;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   int bid = blockIdx.x;
   const int split = bid % a.nsplit;
@@ -364,10 +432,18 @@ __global__ __launch_bounds__(256) void attend_rows_kernel(const AttendArgs a) {
     if (lane == 0) sm.ctx = rs.ctx;
   }
   __syncthreads();
-  const int ctx = sm.ctx;
+  const int ctx = __builtin_amdgcn_readfirstlane(sm.ctx);
   const int nchunks = (ctx + 31) >> 5;
   const int c0 = (int)((int64_t)nchunks * split / a.nsplit);
   const int c1 = (int)((int64_t)nchunks * (split + 1) / a.nsplit);
+
+  // this wave's chunks: cw, cw + 4, cw + 8, ... below c1; NB of them in flight
+  const LaneOffsets lo = lane_offsets<FMT, D>(lane);
+  const int cw = c0 + wave;
+  const int n_w = cw < c1 ? (c1 - cw + 3) >> 2 : 0;
+  ChunkRaw<FMT, D> raw[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) issue_loads<FMT, D, AUX>(raw[b], chunk_loc<FMT, D>(a, sm.slot_list, cw + 4 * b, c1, ctx, kvh), lo);
 
   // Q operand: head kvh*G + r (zero for padded heads r >= G)
   const int G = a.group;
@@ -394,16 +470,20 @@ __global__ __launch_bounds__(256) void attend_rows_kernel(const AttendArgs a) {
   st.lacc = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
 
-  ChunkRaw<FMT, D> raw;
-  int c = c0 + wave;
-  if (c < c1) {
-    const ChunkAddr ca = chunk_addr<FMT>(a, sm.slot_list, c);
-    load_k<FMT, D>(raw, a, ca, c, ctx, kvh, lane);
-    load_v<FMT, D>(raw, a, ca, c, ctx, kvh, lane);
-  }
-  for (; c < c1; c += 4) {
-    const bool ok = chunk_addr<FMT>(a, sm.slot_list, c).ok;
-    process_chunk<FMT, D>(st, raw, qop, sl2, c, ctx, ok, lane, a, sm.slot_list, c + 4, c + 4 < c1, kvh);
+  // Loads are issued unconditionally (past the wave's range they fetch
+  // nothing), so every path has the same outstanding loads and each chunk
+  // waits only for its own.
+  for (int j = 0; j < n_w; j += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c = cw + 4 * (j + b);
+      if (j + b < n_w) {
+        const ChunkLoc L = chunk_loc<FMT, D>(a, sm.slot_list, c, c1, ctx, kvh);
+        const bool masked = !L.ok || c * 32 + 32 > ctx;
+        compute_chunk<FMT, D>(st, raw[b], qop, sl2, masked, c * 32 + 4 * g, L.ok ? ctx : 0);
+      }
+      issue_loads<FMT, D, AUX>(raw[b], chunk_loc<FMT, D>(a, sm.slot_list, c + 4 * NB, c1, ctx, kvh), lo);
+    }
   }
 
   // merge the four waves through LDS
@@ -485,7 +565,21 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const AttendArgs a, i
 template <int FMT, int D, int MODE>
 static hipError_t launch_fmt(const AttendArgs& a, int rows, hipStream_t stream) {
   const int64_t blocks = (int64_t)rows * a.num_kv_heads * a.nsplit;
-  hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  // With one query row per request each page is read by exactly one
+  // workgroup: stream it past the caches.  Several rows of a request (a
+  // multi-token decode, prefill rows) select overlapping blocks, which the
+  // L2 then serves to the neighbouring rows.
+  bool streamed = false;
+  if constexpr (MODE == kModeDecode) {
+    if (a.dql == 1) {
+      hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE, kStreamLoads>), dim3((unsigned)blocks), dim3(256), 0,
+                         stream, a);
+      streamed = true;
+    }
+  }
+  if (!streamed) {
+    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE, 0>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int pairs = rows * a.num_q_heads;
