@@ -57,10 +57,14 @@ __device__ __forceinline__ constexpr int kappa(int kk, int g) {
   }
 }
 
-// Chunks a wave keeps in flight: enough bytes to cover the memory latency
-// within the register budget of two waves per SIMD.
+// Chunks a wave keeps in flight, and waves per SIMD.  bf16 and fp8 pages
+// are bound by HBM: two waves holding 32 KB / 24 KB of loads each.  NVFP4
+// spends more instructions per byte on dequant, so a third wave (and fewer
+// chunks each) hides the dependency stalls better.
 template <int FMT>
-constexpr int kStages = FMT == kFmtBf16 ? 2 : (FMT == kFmtFp8 ? 3 : 4);
+constexpr int kStages = FMT == kFmtBf16 ? 2 : (FMT == kFmtFp8 ? 3 : 2);
+template <int FMT>
+constexpr int kWavesPerSimd = FMT == kFmtNvfp4 ? 3 : 2;
 
 template <int FMT, int D>
 struct ChunkRaw;
@@ -408,7 +412,7 @@ struct AttendSmem {
 };
 
 template <int FMT, int D, int MODE, int AUX>
-__global__ __launch_bounds__(256, 2) void attend_rows_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(const AttendArgs a) {
   constexpr int KK = D / 32, NN = D / 16, NB = kStages<FMT>;
   typedef typename OpType<FMT>::type OT;
   __shared__ AttendSmem<D> sm;

@@ -21,11 +21,9 @@
 // as [d pair of 16-byte chunks][key] so that the transposing read
 // ds_read_b64_tr_b16 (a lane receives one column of the 4 key rows its
 // 16-lane group points at) yields the V^T operand with no bank conflict.
-// The next block's copies are issued in four pieces, one after each 32-key
-// chunk's V reads; the compiler waits for outstanding copies before a
-// transposing read, so each piece has one chunk of compute to land.  Every
-// wave
-// owns 2 matrix tiles of 16 rows = (16 / G query rows) x (G heads) and runs
+// The next block's copies are all issued when a block starts, into the other
+// buffer, so they have the whole block's compute to land.  Every wave owns 2
+// matrix tiles of 16 rows = (16 / G query rows) x (G heads) and runs
 // QK^T and PV only for the tiles whose rows selected the block; the other
 // rows of an active tile are masked.  Online softmax state stays in
 // registers; the workgroup writes its rows' bf16 outputs at the end.
@@ -196,7 +194,8 @@ struct PfNext {       // the block whose copies are issued during this one
 // One selected block against this wave's tiles.  `causal` is set when the
 // block can be the own block of a row of this workgroup (keys past a row's
 // position must be masked); earlier blocks need only the row selection.
-// Every wave issues its pieces of the next block's copies, active or not.
+// Every wave first issues its pieces of the next block's copies, active or
+// not.
 __device__ __forceinline__ void pf_compute_block(PfWave& w, const uint8_t* kb, const uint8_t* vb, uint32_t bmask,
                                                  int blk, int wave, int RT, float sl2, bool causal,
                                                  const PfNext& nx, const AttendArgs& a, int kvh, int seq_len) {
@@ -224,6 +223,10 @@ __device__ __forceinline__ void pf_compute_block(PfWave& w, const uint8_t* kb, c
   const int kpos_blk = blk * kBlockTokens;
   const u32x4 ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 x 8
   const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_w);
+  if (nx.valid) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) pf_issue_part(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len, part);
+  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     bf16x8 kop[2][KK];
@@ -245,7 +248,6 @@ __device__ __forceinline__ void pf_compute_block(PfWave& w, const uint8_t* kb, c
         vop[nn] = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
       }
     }
-    if (nx.valid) pf_issue_part(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len, c);
     if (tiles) {
       const int kbase = kpos_blk + c * 32 + 4 * g;
       if (tiles == 3) pf_chunk<3>(w, kop, vop, bias, ones, sl2, causal, kbase);
