@@ -45,6 +45,18 @@ DESCR = {
 }
 
 
+def workload_key(args):
+    """Config name, with the page format when --kv-dtype overrides it."""
+    return args.config + (f"/{args.kv_dtype}" if args.kv_dtype else "")
+
+
+def describe(args):
+    d = DESCR[args.config]
+    if args.kv_dtype:
+        d = d.replace("bf16", args.kv_dtype).replace("fp8 e4m3", args.kv_dtype).replace("NVFP4", args.kv_dtype)
+    return d
+
+
 def _cpu_baseline(wl, cache, q, ctx, seconds):
     """Time the CPU oracle on rows of the workload until `seconds` pass."""
     import numpy as np
@@ -130,6 +142,7 @@ def summarize(args):
     """Write profiles/<name>.md from rocprofv3 outputs (kernel trace + two counter runs + copy calibration)."""
     import numpy as np
     mode = "prefill" if args.config == "C4" else "decode"
+    cfg_key = workload_key(args)
     key = args.kernel
     stats = [r for r in _read_csv(args.trace_dir) if "Calls" in r and key in r["Name"]]
     trace = [r for r in _read_csv(args.trace_dir) if "Start_Timestamp" in r and key in r.get("Kernel_Name", "")]
@@ -147,12 +160,12 @@ def summarize(args):
     wscale = copy_kib / float(np.median(cwrite))
     fetch_b = float(np.median(fetch)) * 1024 * fscale
     write_b = float(np.median(write)) * 1024 * wscale
-    info = {"config": args.config, "kernel": key, "source_hash": kernel_source_hash(mode),
+    info = {"config": cfg_key, "kernel": key, "source_hash": kernel_source_hash(mode),
             "avg_ns": float(np.mean(durs)), "dispatches": len(durs),
             "fetch_kib_raw": float(np.median(fetch)), "write_kib_raw": float(np.median(write)),
             "fetch_scale": fscale, "write_scale": wscale,
             "traffic_bytes": fetch_b + write_b}
-    lines = [f"# {key}: {args.config} ({DESCR[args.config]})", "",
+    lines = [f"# {key}: {cfg_key} ({describe(args)})", "",
              "Commands (run from the repository root on one MI355X; rocprofv3 writes CSVs):", "",
              "```", *args.commands.split(" ;; "), "```", "",
              f"* kernel dispatches traced: {len(durs)}; average duration {np.mean(durs) / 1e3:.2f} us "
@@ -181,6 +194,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2", choices=sorted(DESCR))
+    ap.add_argument("--kv-dtype", choices=["bf16", "fp8", "nvfp4"], default=None,
+                    help="page format instead of the workload's own (fp8 / NVFP4 prefill)")
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -220,8 +235,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return
-    wl = make_workload(args.config)
-    print(f"[bench] {args.config}: building inputs", file=sys.stderr, flush=True)
+    wl = make_workload(args.config, **({"kv_dtype": args.kv_dtype} if args.kv_dtype else {}))
+    print(f"[bench] {workload_key(args)}: building inputs", file=sys.stderr, flush=True)
     cache = make_kv_cache(wl, dev)
     q = make_query(wl, dev)
     topk = torch.from_numpy(wl.topk).to(dev)
@@ -288,14 +303,14 @@ def main():
         value, unit = work / (ms_per_step * 1e-3) / 1e9, "GB/s"
         achieved = work / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(args.config, "decode")}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(workload_key(args), "decode")}
         dtype = "f16" if wl.kv_dtype == "nvfp4" else "bf16"
     else:
         value, unit = work / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
         achieved = work / (kernel_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(args.config, "prefill")}
-        dtype = "bf16"
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(workload_key(args), "prefill")}
+        dtype = "f16" if wl.kv_dtype == "nvfp4" else "bf16"
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -304,7 +319,7 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
-        "config": {"workload": f"{args.config} {DESCR[args.config]}", "rows": wl.total_q,
+        "config": {"workload": f"{workload_key(args)} {describe(args)}", "rows": wl.total_q,
                    "sum_ctx": sum_ctx, "kernel_ms": kernel_ms, "layers": len(layers)},
         "roofline": roof, "cpu_baseline": cpu,
     }

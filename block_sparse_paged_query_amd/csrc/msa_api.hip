@@ -279,8 +279,6 @@ MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t 
   msa_status_t st = check_attend(q, q_dtype, total_q, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table,
                                  bt_row_stride, bt_cols, out, softmax_scale);
   if (st != MSA_OK) return st;
-  MSA_CHECK(kv->kv_dtype == MSA_BF16, MSA_ERR_UNSUPPORTED, "prefill serves bf16 pages only (got dtype %d)",
-            kv->kv_dtype);
   if (total_q == 0) return ok();
   MSA_CHECK(num_reqs >= 1 && cu_seqlens_q && seq_lens, MSA_ERR_INVALID_ARGUMENT,
             "prefill needs num_reqs >= 1, cu_seqlens_q and seq_lens");
@@ -292,7 +290,7 @@ MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t 
   a.dql = 1;
   a.total_rows = total_q;
   if (msa::prefill_blocks_supported(a.group, kv->head_dim, fmt_of(kv->kv_dtype), bt_cols))
-    return hip_status(msa::launch_prefill_blocks(a, stream), "prefill launch");
+    return hip_status(msa::launch_prefill_blocks(a, fmt_of(kv->kv_dtype), stream), "prefill launch");
   return hip_status(msa::launch_attend_rows(a, fmt_of(kv->kv_dtype), msa::kModePrefill, total_q, stream),
                     "prefill launch");
 }

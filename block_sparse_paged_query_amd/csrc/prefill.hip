@@ -29,6 +29,15 @@
 // registers; the workgroup writes its rows' bf16 outputs at the end.
 // Workgroups of one kv head share an XCD (blockIdx % Hkv), so K/V blocks
 // re-read by neighbouring query tiles hit that XCD's L2.
+//
+// fp8 and NVFP4 pages ([FI] forward folds the fp8 scales; [NV4] customize_spec
+// for the two NVFP4 slots) take a staged path: the selected block's raw bytes
+// (half or a quarter of bf16's) go into a double-buffered LDS staging area,
+// and at the start of each block the workgroup converts them exactly (fp8 ->
+// bf16; e2m1 x E4M3 block scale -> fp16) into the same K / V layouts the
+// bf16 path reads, so the matrix-core loop is shared.  NVFP4 computes in
+// fp16 (the query is converted once), fp8 in bf16; the per-tensor scales
+// fold into the softmax scale and the output as in the decode.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -39,6 +48,14 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfTiles = 2;                 // matrix tiles per wave
 constexpr int kPfMaxBlocks = 2048;          // request blocks a workgroup can index
 constexpr int kPfBlockBytes = kBlockTokens * 256;   // one block of K (or V), bf16, head_dim 128
+// raw bytes of one block (one kv head, K and V) in the staging buffers
+constexpr int kPfFp8RawBytes = 2 * kBlockTokens * 128;               // [key][128] K, then [16-byte piece][key] V
+constexpr int kPfNvfp4RawBytes = kPagesPerBlock * 2 * 9 * 128;       // per page: K slot, V slot (1152 B each)
+template <int FMT>
+constexpr int kPfRawBytes = FMT == kFmtBf16 ? kPfBlockBytes : (FMT == kFmtFp8 ? kPfFp8RawBytes : kPfNvfp4RawBytes);
+// compute operand type: bf16 for bf16 / fp8 pages, fp16 for NVFP4 pages
+template <int FMT> struct PfOp { typedef bf16x8 type; };
+template <> struct PfOp<kFmtNvfp4> { typedef f16x8 type; };
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -93,9 +110,10 @@ __device__ __forceinline__ void pf_issue_part(lds_u8* kb, lds_u8* vb, const Atte
   }
 }
 
+template <class OT>
 struct PfWave {
   static constexpr int KK = 4, NN = 8;
-  bf16x8 qop[kPfTiles][KK];
+  OT qop[kPfTiles][KK];
   f32x4 acc[kPfTiles][NN];
   f32x4 lacc[kPfTiles];   // softmax denominators: P times an all-ones operand
   float m[kPfTiles];
@@ -116,11 +134,12 @@ constexpr float kLazy = 8.f;
 // softmaxes (one uniform branch covers the rare rescale of any tile), then all
 // PV products.  A tile's softmax runs while the next tile's products are in
 // the matrix pipe, and its PV products while the next softmax runs.
-template <int MASK>
-__device__ __forceinline__ void pf_chunk(PfWave& w, const bf16x8 (&kop)[2][PfWave::KK], const bf16x8 (&vop)[PfWave::NN],
-                                         const float (&bias)[kPfTiles], const bf16x8& ones, float sl2, bool causal,
+template <int MASK, class OT>
+__device__ __forceinline__ void pf_chunk(PfWave<OT>& w, const OT (&kop)[2][PfWave<OT>::KK], const OT (&vop)[PfWave<OT>::NN],
+                                         const float (&bias)[kPfTiles], const OT& ones, float sl2, bool causal,
                                          int kbase) {
-  constexpr int KK = PfWave::KK, NN = PfWave::NN;
+  constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
+  constexpr bool kF16 = __is_same(OT, f16x8);
   float sv[kPfTiles][8];
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
@@ -176,8 +195,13 @@ __device__ __forceinline__ void pf_chunk(PfWave& w, const bf16x8 (&kop)[2][PfWav
     float p[8];
 #pragma unroll
     for (int ii = 0; ii < 8; ++ii) p[ii] = exp2_fast(fmaf(sv[i][ii], sl2, off));
-    const u32x4 pw = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+    u32x4 pw;
+    if constexpr (kF16) {
+      pw = u32x4{pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]), pack_f16(p[6], p[7])};
+    } else {
+      pw = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+    }
+    const OT pop = __builtin_bit_cast(OT, pw);
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = mfma16(vop[nn], pop, w.acc[i][nn]);
     w.lacc[i] = mfma16(ones, pop, w.lacc[i]);
@@ -196,10 +220,12 @@ struct PfNext {       // the block whose copies are issued during this one
 // position must be masked); earlier blocks need only the row selection.
 // Every wave first issues its pieces of the next block's copies, active or
 // not.
-__device__ __forceinline__ void pf_compute_block(PfWave& w, const uint8_t* kb, const uint8_t* vb, uint32_t bmask,
+template <class OT>
+__device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* kb, const uint8_t* vb, uint32_t bmask,
                                                  int blk, int wave, int RT, float sl2, bool causal,
                                                  const PfNext& nx, const AttendArgs& a, int kvh, int seq_len) {
-  constexpr int KK = PfWave::KK, NN = PfWave::NN;
+  constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
+  constexpr bool kF16 = __is_same(OT, f16x8);
   static_assert(kPfTiles == 2, "the tile sets below enumerate two tiles");
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   // per-lane LDS offsets (chunk / tile / step parts are compile-time)
@@ -221,23 +247,23 @@ __device__ __forceinline__ void pf_compute_block(PfWave& w, const uint8_t* kb, c
     bias[i] = sel ? 0.f : -INFINITY;
   }
   const int kpos_blk = blk * kBlockTokens;
-  const u32x4 ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 x 8
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_w);
+  const uint32_t one2 = kF16 ? 0x3c003c00u : 0x3f803f80u;   // 1.0 x 2 in the operand type
+  const OT ones = __builtin_bit_cast(OT, u32x4{one2, one2, one2, one2});
   if (nx.valid) {
 #pragma unroll
     for (int part = 0; part < 4; ++part) pf_issue_part(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len, part);
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    bf16x8 kop[2][KK];
-    bf16x8 vop[NN];
+    OT kop[2][KK];
+    OT vop[NN];
     if (tiles) {
       // operands of this 32-key chunk, shared by the wave's active tiles
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          kop[tt][kk] = *reinterpret_cast<const bf16x8*>(kb + (c * 32 + 16 * tt) * 256 + koff[kk]);
+          kop[tt][kk] = *reinterpret_cast<const OT*>(kb + (c * 32 + 16 * tt) * 256 + koff[kk]);
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) {
         const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -245,24 +271,130 @@ __device__ __forceinline__ void pf_compute_block(PfWave& w, const uint8_t* kb, c
         const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (v4i16 __attribute__((address_space(3)))*)((const lds_u8*)vb + nn * 4096 + c * 1024 + 512 + voff));
         const u32x2 l0 = __builtin_bit_cast(u32x2, h0), l1 = __builtin_bit_cast(u32x2, h1);
-        vop[nn] = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
+        vop[nn] = __builtin_bit_cast(OT, u32x4{l0[0], l0[1], l1[0], l1[1]});
       }
     }
     if (tiles) {
       const int kbase = kpos_blk + c * 32 + 4 * g;
-      if (tiles == 3) pf_chunk<3>(w, kop, vop, bias, ones, sl2, causal, kbase);
-      else if (tiles == 1) pf_chunk<1>(w, kop, vop, bias, ones, sl2, causal, kbase);
-      else pf_chunk<2>(w, kop, vop, bias, ones, sl2, causal, kbase);
+      if (tiles == 3) pf_chunk<3, OT>(w, kop, vop, bias, ones, sl2, causal, kbase);
+      else if (tiles == 1) pf_chunk<1, OT>(w, kop, vop, bias, ones, sl2, causal, kbase);
+      else pf_chunk<2, OT>(w, kop, vop, bias, ones, sl2, causal, kbase);
     }
   }
 }
 
+// ---- staged formats -------------------------------------------------------
+//
+// Copy of one block's raw bytes (kv head kvh) into the staging buffer `raw`,
+// spread over the workgroup: each wave instruction fills 64 consecutive
+// 16-byte slots, a lane's source being any 16-byte piece.
+//   fp8:   K as [key][128 B] (piece (key, n) at key * 8 + n), then V as
+//          [n][key] (piece at 1024 + n * 128 + key) so that the conversion
+//          writes the V layout with consecutive lanes on consecutive keys.
+//   NVFP4: the block's 8 pages, each the K slot then the V slot of kvh
+//          (2 x 1152 B, adjacent in the page), piece q at q.
+template <int FMT>
+__device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a, int kvh, int phys) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t pg = (int64_t)phys * a.block_page_stride;
+  if constexpr (FMT == kFmtFp8) {
+    const int64_t head_off = (int64_t)kvh * kPageTokens * 128;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = k * kPfThreads + wave * 64 + lane;
+      const uint8_t* src;
+      if (k < 2) {
+        const int key = q >> 3, n = q & 7;
+        src = a.k_base + (pg + (key >> 4)) * a.page_stride + head_off + (key & 15) * 128 + 16 * n;
+      } else {
+        const int q2 = q - 1024, n = q2 >> 7, key = q2 & 127;
+        src = a.v_base + (pg + a.v_page_offset + (key >> 4)) * a.page_stride + head_off + (key & 15) * 128 + 16 * n;
+      }
+      __builtin_amdgcn_global_load_lds(src, raw + (k * kPfThreads + wave * 64) * 16, 16, 0, 0);
+    }
+  } else {
+    constexpr int SLOT = 9 * 128, PAGE_PIECES = 2 * SLOT / 16;   // 144 pieces of 16 B per page
+    const int64_t head_off = (int64_t)(2 * kvh) * SLOT;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      if (k == 2 && wave >= 2) break;   // 1152 pieces: the third pass is two waves
+      const int q = k * kPfThreads + wave * 64 + lane;
+      const int page = q / PAGE_PIECES, off = (q - page * PAGE_PIECES) * 16;
+      __builtin_amdgcn_global_load_lds(a.k_base + (pg + page) * a.page_stride + head_off + off,
+                                       raw + (k * kPfThreads + wave * 64) * 16, 16, 0, 0);
+    }
+  }
+}
+
+// Exact conversion of a staged block into the compute layouts (K rows with
+// 16-byte chunks swizzled by key; V as ((lc / 2) * 128 + key) * 2 + lc % 2):
+// item (key, n) is the 16 elements d = 16 n .. 16 n + 15, i.e. chunks 2n and
+// 2n + 1.  Keys at or past `nkeys` (the request's end, in its last block)
+// become zeros, which the causal mask gives probability zero.
+template <int FMT>
+__device__ __forceinline__ void pf_stage_item(const uint8_t* raw, bool v_side, int key, int n, uint32_t out[8]) {
+  if constexpr (FMT == kFmtFp8) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(raw + (v_side ? 16384 + (n * 128 + key) * 16 : key * 128 + 16 * n));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = fp8x2_to_bf16x2<false>(w[i]);
+      out[2 * i + 1] = fp8x2_to_bf16x2<true>(w[i]);
+    }
+  } else {
+    constexpr int SLOT = 9 * 128;
+    const uint8_t* slot = raw + (key >> 4) * (2 * SLOT) + (v_side ? SLOT : 0);
+    const int tok = key & 15;
+    const u32x2 w = *reinterpret_cast<const u32x2*>(slot + tok * 64 + 8 * n);
+    const f16x2 sc = fp8x2_to_f16x2<false>((uint32_t)slot[1024 + tok * 8 + n]);
+    const f16x2 s2 = {sc[0], sc[0]};
+    out[0] = f16x2_bits(fp4x2_to_f16x2<0>(w[0]) * s2);
+    out[1] = f16x2_bits(fp4x2_to_f16x2<1>(w[0]) * s2);
+    out[2] = f16x2_bits(fp4x2_to_f16x2<2>(w[0]) * s2);
+    out[3] = f16x2_bits(fp4x2_to_f16x2<3>(w[0]) * s2);
+    out[4] = f16x2_bits(fp4x2_to_f16x2<0>(w[1]) * s2);
+    out[5] = f16x2_bits(fp4x2_to_f16x2<1>(w[1]) * s2);
+    out[6] = f16x2_bits(fp4x2_to_f16x2<2>(w[1]) * s2);
+    out[7] = f16x2_bits(fp4x2_to_f16x2<3>(w[1]) * s2);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void pf_stage_convert(const uint8_t* raw, uint8_t* kc, uint8_t* vc, int nkeys) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = k * kPfThreads + tid;
+    const bool v_side = k >= 2;
+    const int key = v_side ? ((q - 1024) & 127) : (q >> 3);
+    const int n = v_side ? ((q - 1024) >> 7) : (q & 7);
+    uint32_t o[8];
+    pf_stage_item<FMT>(raw, v_side, key, n, o);
+    if (key >= nkeys) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = 0u;
+    }
+    const u32x4 c0 = {o[0], o[1], o[2], o[3]}, c1 = {o[4], o[5], o[6], o[7]};
+    if (!v_side) {
+      const int sw = key & 15;   // chunk c of the key row sits at c ^ (key & 15)
+      *reinterpret_cast<u32x4*>(kc + key * 256 + (((2 * n) ^ sw) << 4)) = c0;
+      *reinterpret_cast<u32x4*>(kc + key * 256 + (((2 * n + 1) ^ sw) << 4)) = c1;
+    } else {
+      *reinterpret_cast<u32x4*>(vc + (n * 128 + key) * 32) = c0;
+      *reinterpret_cast<u32x4*>(vc + (n * 128 + key) * 32 + 16) = c1;
+    }
+  }
+}
+
+template <int FMT>
 __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const AttendArgs a, int n_slots) {
-  constexpr int D = 128, KK = PfWave::KK, NN = PfWave::NN;
-  // two K/V buffers as distinct LDS objects: the loop below is unrolled by two,
-  // so the compiler knows the in-flight copies target the other buffer
-  __shared__ __align__(16) uint8_t k0[kPfBlockBytes], k1[kPfBlockBytes];
-  __shared__ __align__(16) uint8_t v0[kPfBlockBytes], v1[kPfBlockBytes];
+  typedef typename PfOp<FMT>::type OT;
+  constexpr int D = 128, KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
+  // Four LDS buffers as distinct objects: the loops below are unrolled by two,
+  // so the compiler knows the in-flight copies target another buffer.
+  //   bf16:        K / V double buffers (bA, bC) and (bB, bD)
+  //   fp8 / NVFP4: compute K, V (bA, bB) and raw staging buffers bC, bD
+  __shared__ __align__(16) uint8_t bA[kPfBlockBytes], bB[kPfBlockBytes];
+  __shared__ __align__(16) uint8_t bC[kPfRawBytes<FMT>], bD[kPfRawBytes<FMT>];
   __shared__ uint32_t s_mask[kPfMaxBlocks];
   __shared__ uint16_t s_list[kPfMaxBlocks];   // selected blocks, ascending
   __shared__ int32_t s_phys[kPfMaxBlocks];    // their physical block ids
@@ -363,7 +495,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   }
 
   // ---- this wave's query operands and row data
-  PfWave w;
+  PfWave<OT> w;
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
     const int rr = (wave * kPfTiles + i) * RT + r / G;
@@ -376,8 +508,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
                           (((int64_t)(row0 + (ok ? rr : 0)) * a.num_q_heads + kvh * G + (r % G)) * D) * 2;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 q4 = ok ? *reinterpret_cast<const u32x4*>(qrow + 2 * (32 * kk + 8 * g)) : u32x4{0u, 0u, 0u, 0u};
-      w.qop[i][kk] = __builtin_bit_cast(bf16x8, q4);
+      u32x4 q4 = ok ? *reinterpret_cast<const u32x4*>(qrow + 2 * (32 * kk + 8 * g)) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (FMT == kFmtNvfp4) {
+        q4 = u32x4{bf16x2_to_f16x2(q4[0]), bf16x2_to_f16x2(q4[1]), bf16x2_to_f16x2(q4[2]), bf16x2_to_f16x2(q4[3])};
+      }
+      w.qop[i][kk] = __builtin_bit_cast(OT, q4);
     }
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -387,36 +522,67 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   __syncthreads();
   const int n_act = s_info[0];
 
-  if (n_act > 0) {
-#pragma unroll
-    for (int part = 0; part < 4; ++part)
-      pf_issue_part((lds_u8*)k0, (lds_u8*)v0, a, kvh, s_phys[0], s_list[0], seq_len, part);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   const uint32_t wave_bits = ((1u << (kPfTiles * RT)) - 1u) << (wave * kPfTiles * RT);
   const int own_first = pos_first / kBlockTokens;   // blocks before it are wholly in every row's past
-  for (int it = 0; it < n_act; it += 2) {
-    // even step: block in (k0, v0); the next one goes to (k1, v1)
-    {
-      const int j = s_list[it];
-      const PfNext nx = {(lds_u8*)k1, (lds_u8*)v1, it + 1 < n_act ? s_phys[it + 1] : 0,
-                         it + 1 < n_act ? (int)s_list[it + 1] : 0, it + 1 < n_act};
-      const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-      pf_compute_block(w, k0, v0, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
-      __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
-      __syncthreads();
+  if constexpr (FMT == kFmtBf16) {
+    lds_u8 *k0 = (lds_u8*)bA, *k1 = (lds_u8*)bB, *v0 = (lds_u8*)bC, *v1 = (lds_u8*)bD;
+    if (n_act > 0) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) pf_issue_part(k0, v0, a, kvh, s_phys[0], s_list[0], seq_len, part);
     }
-    if (it + 1 >= n_act) break;
-    // odd step: block in (k1, v1); the next one goes to (k0, v0)
-    {
-      const int j = s_list[it + 1];
-      const PfNext nx = {(lds_u8*)k0, (lds_u8*)v0, it + 2 < n_act ? s_phys[it + 2] : 0,
-                         it + 2 < n_act ? (int)s_list[it + 2] : 0, it + 2 < n_act};
-      const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-      pf_compute_block(w, k1, v1, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int it = 0; it < n_act; it += 2) {
+      // even step: block in (k0, v0); the next one goes to (k1, v1)
+      {
+        const int j = s_list[it];
+        const PfNext nx = {k1, v1, it + 1 < n_act ? s_phys[it + 1] : 0, it + 1 < n_act ? (int)s_list[it + 1] : 0,
+                           it + 1 < n_act};
+        const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
+        pf_compute_block<OT>(w, bA, bC, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
+        __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
+        __syncthreads();
+      }
+      if (it + 1 >= n_act) break;
+      // odd step: block in (k1, v1); the next one goes to (k0, v0)
+      {
+        const int j = s_list[it + 1];
+        const PfNext nx = {k0, v0, it + 2 < n_act ? s_phys[it + 2] : 0, it + 2 < n_act ? (int)s_list[it + 2] : 0,
+                           it + 2 < n_act};
+        const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
+        pf_compute_block<OT>(w, bB, bD, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  } else {
+    // staged: raw block in bC / bD (alternating), converted into (bA, bB)
+    const PfNext none = {nullptr, nullptr, 0, 0, false};
+    if (n_act > 0) pf_stage_issue<FMT>((lds_u8*)bC, a, kvh, s_phys[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int it = 0; it < n_act; it += 2) {
+      {
+        const int j = s_list[it];
+        pf_stage_convert<FMT>(bC, bA, bB, seq_len - j * kBlockTokens);
+        __syncthreads();
+        if (it + 1 < n_act) pf_stage_issue<FMT>((lds_u8*)bD, a, kvh, s_phys[it + 1]);
+        const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
+        pf_compute_block<OT>(w, bA, bB, bmask, j, wave, RT, sl2, j >= own_first, none, a, kvh, seq_len);
+        __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
+        __syncthreads();                 // and every wave is done with (bA, bB)
+      }
+      if (it + 1 >= n_act) break;
+      {
+        const int j = s_list[it + 1];
+        pf_stage_convert<FMT>(bD, bA, bB, seq_len - j * kBlockTokens);
+        __syncthreads();
+        if (it + 2 < n_act) pf_stage_issue<FMT>((lds_u8*)bC, a, kvh, s_phys[it + 2]);
+        const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
+        pf_compute_block<OT>(w, bA, bB, bmask, j, wave, RT, sl2, j >= own_first, none, a, kvh, seq_len);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
     }
   }
 
@@ -439,16 +605,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   }
 }
 
-hipError_t launch_prefill_blocks(const AttendArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t stream) {
   const int QT = kPfWaves * kPfTiles * (16 / a.group);
   const int n_slots = (a.total_rows + QT - 1) / QT + a.num_reqs + 1;
   const int64_t blocks = (int64_t)n_slots * a.num_kv_heads;
-  hipLaunchKernelGGL(prefill_blocks_kernel, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a, n_slots);
+  if (fmt == kFmtBf16) {
+    hipLaunchKernelGGL(prefill_blocks_kernel<kFmtBf16>, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a, n_slots);
+  } else if (fmt == kFmtFp8) {
+    hipLaunchKernelGGL(prefill_blocks_kernel<kFmtFp8>, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a, n_slots);
+  } else {
+    hipLaunchKernelGGL(prefill_blocks_kernel<kFmtNvfp4>, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a,
+                       n_slots);
+  }
   return hipGetLastError();
 }
 
 bool prefill_blocks_supported(int group, int head_dim, int fmt, int bt_cols) {
-  return (group == 8 || group == 16) && head_dim == 128 && fmt == kFmtBf16 && bt_cols <= kPfMaxBlocks;
+  return (group == 8 || group == 16) && head_dim == 128 && bt_cols <= kPfMaxBlocks;
 }
 
 }  // namespace msa

@@ -205,8 +205,9 @@ MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, 
  * cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 are request r's new tokens, at
  * positions seq_lens[r] - (cu_seqlens_q[r+1] - cu_seqlens_q[r]) + local
  * offset (seq_lens counts the new tokens); rows >= cu_seqlens_q[num_reqs]
- * are padding and get 0.  Same math and limits as msa_sparse_decode;
- * kv_dtype must be MSA_BF16 today.
+ * are padding and get 0.  Same math, page formats and limits as
+ * msa_sparse_decode (bf16, fp8 e4m3fn or NVFP4 pages; NVFP4 computes in
+ * fp16).
  */
 MSA_API msa_status_t msa_sparse_prefill(
     const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,

@@ -108,11 +108,16 @@ def test_decode_empty_batch_is_noop():
     assert _decode(_kv(), num_reqs=0) == 0
 
 
-def test_prefill_rejects_fp8_pages():
+def test_prefill_rejects_unsupported_shapes():
+    # validation runs before any HIP call, so fake device pointers are safe
     kv = _kv(kv_dtype=msa.MSA_FP8_E4M3FN, page_stride_bytes=8 * 16 * 128)
-    st = _lib().msa_sparse_prefill(FAKE, 0, 10, 64, ctypes.byref(kv), FAKE, 16, 16, FAKE, 64, 64, 1, FAKE, FAKE,
-                                   0.1, FAKE, None, 0, None)
-    assert st == 2
+    fp16_q = _lib().msa_sparse_prefill(FAKE, 1, 10, 64, ctypes.byref(kv), FAKE, 16, 16, FAKE, 64, 64, 1, FAKE, FAKE,
+                                       0.1, FAKE, None, 0, None)
+    assert fp16_q == 2
+    kv96 = _kv(head_dim=96, page_stride_bytes=8 * 16 * 96 * 2)
+    d96 = _lib().msa_sparse_prefill(FAKE, 0, 10, 64, ctypes.byref(kv96), FAKE, 16, 16, FAKE, 64, 64, 1, FAKE, FAKE,
+                                    0.1, FAKE, None, 0, None)
+    assert d96 == 2
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

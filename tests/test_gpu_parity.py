@@ -182,6 +182,16 @@ def test_prefill_parity_small():
     dict(block_page_stride=16, seed=44),                 # K and V sides in one block
     dict(qlens=[1, 40, 700], context=[3000, 0, 129], seed=45),   # long context, tiny request
     dict(qlens=[0, 300], context=[50, 0], seed=46),      # an empty request
+    # fp8 and NVFP4 pages: raw blocks staged in LDS and converted for the matrix cores
+    dict(kv_dtype="fp8", seed=47),
+    dict(kv_dtype="nvfp4", seed=48),
+    dict(kv_dtype="fp8", Hq=32, Hkv=2, seed=49),
+    dict(kv_dtype="nvfp4", Hq=32, Hkv=2, seed=53),
+    dict(kv_dtype="fp8", block_page_stride=16, seed=50),
+    dict(kv_dtype="nvfp4", qlens=[1, 40, 700], context=[3000, 0, 129], seed=51),
+    dict(kv_dtype="fp8", qlens=[0, 300], context=[50, 0], seed=54),
+    dict(kv_dtype="fp8", Hq=16, Hkv=4, seed=52),         # 4 per kv head: row-wise path
+    dict(kv_dtype="nvfp4", Hq=16, Hkv=4, seed=55),       # 4 per kv head: row-wise path
 ])
 def test_prefill_parity_variants(kw):
     _parity(make_workload("C4s", **kw))
@@ -196,8 +206,9 @@ def test_decode_parity_full_size_sampled(name, rows):
     _parity(make_workload(name), rows)
 
 
-def test_prefill_parity_full_size_sampled():
-    wl = make_workload("C4")
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "nvfp4"])
+def test_prefill_parity_full_size_sampled(kv_dtype):
+    wl = make_workload("C4", kv_dtype=kv_dtype)
     rows = [0, 127, 128, 2047, 2048, 6000, 14335, 14336, 22527, 22528, 22591]
     _parity(wl, rows)
 
