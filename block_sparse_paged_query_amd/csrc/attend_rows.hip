@@ -11,11 +11,12 @@
 // [SPA] vllm.models.minimax_m3.amd.ops.sparse_pa,
 //      _write_sparse_block_table_row_from_values: which tokens a row sees.
 //
-// Work decomposition.  One workgroup (4 waves) owns (row, kv head, split).
-// Wave 0 compacts the row's top-k ids into the slot list (full blocks, then
-// the causal tail) in LDS.  The row's context [0, ctx) is cut into 32-token
-// chunks (two 16-token pages of one 128-token block); a split owns a
-// contiguous range of chunks and its four waves take every fourth chunk.
+// Work decomposition.  One workgroup (W = 2..4 waves, chosen at launch so
+// that the grid fills whole rounds of the machine) owns (row, kv head,
+// split).  Wave 0 compacts the row's top-k ids into the slot list (full
+// blocks, then the causal tail) in LDS.  The row's context [0, ctx) is cut
+// into 32-token chunks (two 16-token pages of one 128-token block); a split
+// owns a contiguous range of chunks and its W waves take every W-th chunk.
 // Each wave keeps its own online-softmax state and several chunks' loads in
 // flight; the four states are merged through LDS at the end.  With one split
 // the workgroup writes the bf16 output directly; otherwise it writes an fp32
@@ -38,6 +39,8 @@
 //              lane loads 8 token rows of NN consecutive elements and
 //              transposes them in registers (no LDS round trip)
 //   O output:  head r, d = (4g+i)*NN + nn, i.e. 4*NN consecutive d per lane.
+#include <algorithm>
+
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -83,7 +86,7 @@ struct ChunkRaw<kFmtFp8, D> {
   u32x4 k[2][KK / 2];      // tile t: 16 codes per load = two steps
   uint32_t v[8][NN / 4];   // row i: NN codes
 };
-// NVFP4 slots: per token D/2 code bytes, then per token D/16 scale bytes.
+// NVFP4 slots (byte order in msa_device.h): K token-major, V in groups of 4 tokens.
 template <int D>
 struct ChunkRaw<kFmtNvfp4, D> {
   static constexpr int KK = D / 32, NN = D / 16;
@@ -91,7 +94,7 @@ struct ChunkRaw<kFmtNvfp4, D> {
   u32x4 k[2];              // tile t: 32 codes (d in [32g, 32g+32))
   uint32_t ks[2];          // tile t: scales of groups 2g, 2g+1 (low 16 bits)
   uint32_t v[8];           // row i: 8 codes, d in [8r, 8r+8)
-  uint32_t vs[8];          // row i: the scale of group r/2 (low 8 bits)
+  uint32_t vs[2];          // page t: byte i = the scale of group r/2 of token 4g + i
 };
 
 template <class T>
@@ -150,8 +153,8 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   if constexpr (FMT == kFmtNvfp4) {
     o.k = r * (D / 2) + 16 * g;           // 32 codes: d in [32g, 32g + 32)
     o.ks = r * (D / 16) + 2 * g;          // scales of groups 2g and 2g + 1
-    o.v = 4 * g * (D / 2) + 4 * r;        // 8 codes: d in [8r, 8r + 8)
-    o.vs = 4 * g * (D / 16) + (r >> 1);   // the scale of group r / 2
+    o.v = (g * (D / 8) + r) * 16;         // 8 codes (d in [8r, 8r + 8)) of tokens 4g .. 4g+3
+    o.vs = (g * (D / 16) + (r >> 1)) * 4; // their scales of group r / 2
   } else {
     constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1, ROW = D * ESZ, NN = D / 16;
     o.k = r * ROW + 16 * g;
@@ -210,15 +213,21 @@ __device__ __forceinline__ void issue_loads(ChunkRaw<FMT, D>& raw, const ChunkLo
       raw.k[t] = buf_load16<AUX>(kc, o.k);
       raw.ks[t] = buf_load2<AUX>(ksr, o.ks);
     }
+    // V slots interleave the tokens of a group of 4, so a descriptor covers
+    // a whole page whenever any of it is valid; the scales of tokens past the
+    // context are cleared in the context's last chunk instead (codes are
+    // always finite, an unwritten scale byte may not be)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const BufRsrc vc = make_rsrc(L.v[t], L.valid[t] * CODE);
-      const BufRsrc vsr = make_rsrc(L.v[t] + SREG, L.valid[t] * SCALE);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        raw.v[4 * t + i] = buf_load4<AUX>(vc, o.v + i * CODE);
-        raw.vs[4 * t + i] = buf_load1<AUX>(vsr, o.vs + i * SCALE);
-      }
+      const bool any = L.valid[t] > 0;
+      const BufRsrc vc = make_rsrc(L.v[t], any ? kPageTokens * CODE : 0);
+      const BufRsrc vsr = make_rsrc(L.v[t] + SREG, any ? kPageTokens * SCALE : 0);
+      const u32x4 w = buf_load16<AUX>(vc, o.v);
+      raw.v[4 * t + 0] = w[0];
+      raw.v[4 * t + 1] = w[1];
+      raw.v[4 * t + 2] = w[2];
+      raw.v[4 * t + 3] = w[3];
+      raw.vs[t] = buf_load4<AUX>(vsr, o.vs);
     }
   } else {
     constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1, ROW = D * ESZ;
@@ -310,7 +319,8 @@ __device__ __forceinline__ void v_operands(const ChunkRaw<FMT, D>& raw, u32x4 vo
       }
     } else {
       const uint32_t a = raw.v[2 * p], b = raw.v[2 * p + 1];
-      const f16x2 s = fp8x2_to_f16x2<false>(raw.vs[2 * p] | (raw.vs[2 * p + 1] << 8));   // (scale a, scale b)
+      // (scale a, scale b): bytes 2 (p % 2), 2 (p % 2) + 1 of page p / 2's scale word
+      const f16x2 s = (p & 1) ? fp8x2_to_f16x2<true>(raw.vs[p >> 1]) : fp8x2_to_f16x2<false>(raw.vs[p >> 1]);
       // byte j of x: element 2j of a (low nibble) and of b (high nibble); y: element 2j + 1
       const uint32_t x = (a & 0x0f0f0f0fu) | ((b << 4) & 0xf0f0f0f0u);
       const uint32_t y = ((a >> 4) & 0x0f0f0f0fu) | (b & 0xf0f0f0f0u);
@@ -395,7 +405,21 @@ __device__ __forceinline__ void compute_chunk(WaveState<FMT, D>& st, const Chunk
   }
   const OT pop = __builtin_bit_cast(OT, pw);
   u32x4 vop[NN];
-  v_operands<FMT, D>(raw, vop);
+  if constexpr (FMT == kFmtNvfp4) {
+    ChunkRaw<FMT, D> rv = raw;
+    if (masked) {   // clear the V scales of tokens at or past lim (page t, byte i: token tok0 + 16t + i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t keep = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) keep |= (tok0 + 16 * t + i < lim) ? (0xffu << (8 * i)) : 0u;
+        rv.vs[t] &= keep;
+      }
+    }
+    v_operands<FMT, D>(rv, vop);
+  } else {
+    v_operands<FMT, D>(raw, vop);
+  }
 #pragma unroll
   for (int nn = 0; nn < NN; ++nn) st.acc[nn] = mfma16(__builtin_bit_cast(OT, vop[nn]), pop, st.acc[nn]);
   st.lacc = mfma16(__builtin_bit_cast(OT, onesw), pop, st.lacc);
@@ -406,7 +430,7 @@ template <int D>
 struct AttendSmem {
   int slot_list[kMaxTopK];
   int ctx;
-  float m[4][16];
+  float m[4][16];      // per wave (up to 4)
   float l[4][16];
   float o[4][16][D];
 };
@@ -417,6 +441,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   typedef typename OpType<FMT>::type OT;
   __shared__ AttendSmem<D> sm;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nw = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);   // waves of the workgroup (2..4)
   const int r = lane & 15, g = lane >> 4;
   int bid = blockIdx.x;
   const int split = bid % a.nsplit;
@@ -441,13 +466,14 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   const int c0 = (int)((int64_t)nchunks * split / a.nsplit);
   const int c1 = (int)((int64_t)nchunks * (split + 1) / a.nsplit);
 
-  // this wave's chunks: cw, cw + 4, cw + 8, ... below c1; NB of them in flight
+  // this wave's chunks: cw, cw + nw, cw + 2 nw, ... below c1; NB of them in flight
   const LaneOffsets lo = lane_offsets<FMT, D>(lane);
   const int cw = c0 + wave;
-  const int n_w = cw < c1 ? (c1 - cw + 3) >> 2 : 0;
+  const int n_w = cw < c1 ? (c1 - cw + nw - 1) / nw : 0;
   ChunkRaw<FMT, D> raw[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) issue_loads<FMT, D, AUX>(raw[b], chunk_loc<FMT, D>(a, sm.slot_list, cw + 4 * b, c1, ctx, kvh), lo);
+  for (int b = 0; b < NB; ++b)
+    issue_loads<FMT, D, AUX>(raw[b], chunk_loc<FMT, D>(a, sm.slot_list, cw + nw * b, c1, ctx, kvh), lo);
 
   // Q operand: head kvh*G + r (zero for padded heads r >= G)
   const int G = a.group;
@@ -480,17 +506,17 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   for (int j = 0; j < n_w; j += NB) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int c = cw + 4 * (j + b);
+      const int c = cw + nw * (j + b);
       if (j + b < n_w) {
         const ChunkLoc L = chunk_loc<FMT, D>(a, sm.slot_list, c, c1, ctx, kvh);
         const bool masked = !L.ok || c * 32 + 32 > ctx;
         compute_chunk<FMT, D>(st, raw[b], qop, sl2, masked, c * 32 + 4 * g, L.ok ? ctx : 0);
       }
-      issue_loads<FMT, D, AUX>(raw[b], chunk_loc<FMT, D>(a, sm.slot_list, c + 4 * NB, c1, ctx, kvh), lo);
+      issue_loads<FMT, D, AUX>(raw[b], chunk_loc<FMT, D>(a, sm.slot_list, c + nw * NB, c1, ctx, kvh), lo);
     }
   }
 
-  // merge the four waves through LDS
+  // merge the waves through LDS
   const float lsum = st.lacc[0];
   if (r < G) {
     if (g == 0) {
@@ -505,15 +531,17 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   }
   __syncthreads();
   const float vscale = a.v_scale ? *a.v_scale : 1.f;
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += nw * 64) {
     const int h = idx / (D / 4), d = (idx % (D / 4)) * 4;
     float M = sm.m[0][h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm.m[w][h]);
+    for (int w = 1; w < 4; ++w)
+      if (w < nw) M = fmaxf(M, sm.m[w][h]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
+      if (w >= nw) break;
       const float e = exp2_fast(sm.m[w][h] - Mu);
       L += sm.l[w][h] * e;
       o0 += sm.o[w][h][d] * e;
@@ -566,9 +594,29 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const AttendArgs a, i
   dst[1] = pack_bf16(o[2] * inv, o[3] * inv);
 }
 
+// Waves per workgroup: 4 unless fewer waves fill the machine in fewer,
+// fuller rounds.  A CU holds waves_per_simd * 4 waves and at most 4
+// workgroups (LDS); a workgroup of nw waves takes nw of those slots.
+static int choose_waves(int64_t units, int waves_per_simd, int cus) {
+  int best = 4;
+  double best_util = 0.0;
+  for (int nw = 4; nw >= 3; --nw) {
+    const int64_t per_cu = std::min<int64_t>(4, (4 * waves_per_simd) / nw);
+    const int64_t per_round = per_cu * (cus > 0 ? cus : 256);
+    const int64_t rounds = (units + per_round - 1) / per_round;
+    const double util = (double)units / (double)(rounds * per_round);
+    if (util > best_util + 1e-9) {
+      best_util = util;
+      best = nw;
+    }
+  }
+  return best;
+}
+
 template <int FMT, int D, int MODE>
 static hipError_t launch_fmt(const AttendArgs& a, int rows, hipStream_t stream) {
   const int64_t blocks = (int64_t)rows * a.num_kv_heads * a.nsplit;
+  const int nw = choose_waves(blocks, kWavesPerSimd<FMT>, a.num_cus);
   // With one query row per request each page is read by exactly one
   // workgroup: stream it past the caches.  Several rows of a request (a
   // multi-token decode, prefill rows) select overlapping blocks, which the
@@ -576,13 +624,13 @@ static hipError_t launch_fmt(const AttendArgs& a, int rows, hipStream_t stream) 
   bool streamed = false;
   if constexpr (MODE == kModeDecode) {
     if (a.dql == 1) {
-      hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE, kStreamLoads>), dim3((unsigned)blocks), dim3(256), 0,
+      hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE, kStreamLoads>), dim3((unsigned)blocks), dim3(64 * nw), 0,
                          stream, a);
       streamed = true;
     }
   }
   if (!streamed) {
-    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE, 0>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE, 0>), dim3((unsigned)blocks), dim3(64 * nw), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;

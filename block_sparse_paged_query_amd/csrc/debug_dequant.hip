@@ -13,7 +13,7 @@
 
 namespace msa {
 
-__device__ __forceinline__ void dequant_pair(int fmt, const uint8_t* page_head, int slot, int D, int e,
+__device__ __forceinline__ void dequant_pair(int fmt, const uint8_t* page_head, bool v_side, int slot, int D, int e,
                                              float* x0, float* x1) {
   if (fmt == kFmtBf16) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(page_head + (slot * D + e) * 2);
@@ -25,9 +25,9 @@ __device__ __forceinline__ void dequant_pair(int fmt, const uint8_t* page_head, 
     *x0 = __uint_as_float(b << 16);
     *x1 = __uint_as_float(b & 0xffff0000u);
   } else {
-    // page_head points at the slot: codes, then scales
-    const uint32_t code = page_head[slot * (D / 2) + e / 2];
-    const uint32_t sb = page_head[kPageTokens * (D / 2) + slot * (D / 16) + e / 16];
+    // page_head points at the slot (head_dim 128): codes, then scales
+    const uint32_t code = page_head[nvfp4_code_byte(v_side, slot, e / 2)];
+    const uint32_t sb = page_head[nvfp4_scale_byte(v_side, slot, e / 16)];
     const f16x2 sc = fp8x2_to_f16x2<false>(sb);
     const f16x2 s = {sc[0], sc[0]};
     const f16x2 v = fp4x2_to_f16x2<0>(code) * s;
@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const DequantArgs a)
     vh = a.v_base + vpage * a.page_stride + (int64_t)h * kPageTokens * D * esz;
   }
   float x0, x1;
-  dequant_pair(a.fmt, kh, slot, D, e, &x0, &x1);
+  dequant_pair(a.fmt, kh, false, slot, D, e, &x0, &x1);
   ko[0] = x0 * ks;
   ko[1] = x1 * ks;
-  dequant_pair(a.fmt, vh, slot, D, e, &x0, &x1);
+  dequant_pair(a.fmt, vh, true, slot, D, e, &x0, &x1);
   vo[0] = x0 * vs;
   vo[1] = x1 * vs;
 }

@@ -89,6 +89,19 @@ msa_status_t check_attend(const void* q, int32_t q_dtype, int32_t rows, int32_t 
   return MSA_OK;
 }
 
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 msa::AttendArgs attend_args(const void* q, int32_t num_q_heads, const msa_kv_cache_t* kv, const int32_t* topk,
                             int64_t topk_row_stride, int32_t topk_k, const int32_t* block_table, int64_t bt_row_stride,
                             int32_t bt_cols, float softmax_scale, void* out) {
@@ -116,6 +129,7 @@ msa::AttendArgs attend_args(const void* q, int32_t num_q_heads, const msa_kv_cac
   a.group = num_q_heads / kv->num_kv_heads;
   a.head_dim = kv->head_dim;
   a.nsplit = 1;
+  a.num_cus = device_cus();
   return a;
 }
 
@@ -123,18 +137,6 @@ size_t split_bytes(int64_t rows, int32_t num_q_heads, int32_t head_dim, int32_t 
   return (size_t)(rows * num_q_heads * nsplit) * (size_t)(head_dim + 2) * sizeof(float) + 256;
 }
 
-int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 // Splits per (row, kv head): enough workgroups for two per compute unit, each
 // split keeping at least one 128-token block per wave.

@@ -90,6 +90,27 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
+// NVFP4 slot byte order, head_dim 128 ([NV4] customize_spec leaves the bytes
+// inside a page to the kernels).  A slot holds 16 tokens: 1024 code bytes
+// (two e2m1 codes per byte, the low nibble the even element), then 128
+// E4M3FN scale bytes (one per 16 elements).
+//   K slot, token-major: code byte c of token t at t * 64 + c, scale u at
+//     1024 + t * 8 + u.
+//   V slot, tokens in groups of 4: the 4-byte unit w (elements 8w .. 8w+7) of
+//     token t at ((t / 4 * 16 + w) * 4 + t % 4) * 4, scale u at
+//     1024 + (t / 4 * 8 + u) * 4 + t % 4 -- a decode lane reads its 8 elements
+//     of 4 tokens (16 bytes) and their 4 scales (4 bytes) in one load each.
+// ---------------------------------------------------------------------------
+constexpr int kNvfp4SlotBytes = 9 * 128;
+constexpr int kNvfp4ScaleBase = 1024;
+__device__ __forceinline__ int nvfp4_code_byte(bool v_slot, int t, int c) {
+  return v_slot ? ((t / 4 * 16 + c / 4) * 4 + t % 4) * 4 + c % 4 : t * 64 + c;
+}
+__device__ __forceinline__ int nvfp4_scale_byte(bool v_slot, int t, int u) {
+  return kNvfp4ScaleBase + (v_slot ? (t / 4 * 8 + u) * 4 + t % 4 : t * 8 + u);
+}
+
+// ---------------------------------------------------------------------------
 // Row compaction ([SPA] _write_sparse_block_table_row_from_values).
 //
 // Run by all 64 lanes of one wave.  Keeps the ids 0 <= id <= own block

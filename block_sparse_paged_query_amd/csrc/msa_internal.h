@@ -39,6 +39,7 @@ struct AttendArgs {
   int32_t total_rows;
   float* ws_o;    // [rows][Hq][nsplit][D]
   float* ws_ml;   // [rows][Hq][nsplit][2]
+  int32_t num_cus;   // compute units of the device (launch shaping)
 };
 
 hipError_t launch_attend_rows(const AttendArgs& a, int fmt, int mode, int rows, hipStream_t stream);

@@ -341,11 +341,12 @@ __device__ __forceinline__ void pf_stage_item(const uint8_t* raw, bool v_side, i
       out[2 * i + 1] = fp8x2_to_bf16x2<true>(w[i]);
     }
   } else {
-    constexpr int SLOT = 9 * 128;
-    const uint8_t* slot = raw + (key >> 4) * (2 * SLOT) + (v_side ? SLOT : 0);
+    const uint8_t* slot = raw + (key >> 4) * (2 * kNvfp4SlotBytes) + (v_side ? kNvfp4SlotBytes : 0);
     const int tok = key & 15;
-    const u32x2 w = *reinterpret_cast<const u32x2*>(slot + tok * 64 + 8 * n);
-    const f16x2 sc = fp8x2_to_f16x2<false>((uint32_t)slot[1024 + tok * 8 + n]);
+    // code bytes 8n .. 8n+7 (elements 16n .. 16n+15): two 4-byte units
+    const u32x2 w = {*reinterpret_cast<const uint32_t*>(slot + nvfp4_code_byte(v_side, tok, 8 * n)),
+                     *reinterpret_cast<const uint32_t*>(slot + nvfp4_code_byte(v_side, tok, 8 * n + 4))};
+    const f16x2 sc = fp8x2_to_f16x2<false>((uint32_t)slot[nvfp4_scale_byte(v_side, tok, n)]);
     const f16x2 s2 = {sc[0], sc[0]};
     out[0] = f16x2_bits(fp4x2_to_f16x2<0>(w[0]) * s2);
     out[1] = f16x2_bits(fp4x2_to_f16x2<1>(w[0]) * s2);

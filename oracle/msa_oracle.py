@@ -216,26 +216,42 @@ def e2m1_value(nib):
     return np.where(s == 1, -mag, mag)
 
 
-def nvfp4_token_values(slot_bytes, token, head_dim, global_scale):
+def nvfp4_token_values(slot_bytes, token, head_dim, global_scale, side="k"):
     """Decode tokens of NVFP4 (page, head-slot) byte rows -> [..., head_dim] fp64.
 
     ``slot_bytes`` [..., 9 * head_dim] uint8 are whole slots and ``token``
-    [...] the token (0..15) to read from each.
+    [...] the token (0..15) to read from each; ``side`` says whether the slot
+    is a K slot ("k") or a V slot ("v").
     [NV4] customize_spec: each head's K and V are two slots of packed data
     plus block scales; the bytes inside a page are laid out for the kernels.
-    Reading (our layout): bytes [0, 8*head_dim) hold token t's packed codes at
-    t*head_dim/2 + d//2, low nibble for even d; bytes [8*head_dim, 9*head_dim)
-    hold token t's E4M3FN scale for elements 16u..16u+15 at
-    8*head_dim + t*head_dim/16 + u.  Value = e2m1 * scale * global.
+    Reading (our layout; two e2m1 codes per byte, the low nibble holding the
+    even element; value = e2m1 * E4M3FN scale of the element's group of 16 *
+    global):
+      K slot, token-major: token t's code byte c (elements 2c, 2c+1) at
+        t*head_dim/2 + c; its scale of group u at 8*head_dim + t*head_dim/16 + u.
+      V slot, in groups of 4 tokens: code byte c of token t at
+        ((t//4 * head_dim/8 + c//4) * 4 + t%4) * 4 + c%4  (so the 4-byte units of
+        the 4 tokens of a group that hold the same 8 elements are adjacent);
+        its scale of group u at 8*head_dim + (t//4 * head_dim/16 + u) * 4 + t%4.
     PARITY UNPINNED for the byte order (a convention of ours; the kernels and
     the oracle follow the same written layout).
     """
     raw = np.asarray(slot_bytes, dtype=np.int64)
     t = np.asarray(token, dtype=np.int64)[..., None]
     d = np.arange(head_dim)
-    byte = np.take_along_axis(raw, t * (head_dim // 2) + d // 2, axis=-1)
+    c = d // 2                      # code byte of element d
+    u = d // 16                     # its scale group
+    if side == "k":
+        code_at = t * (head_dim // 2) + c
+        scale_at = PAGE_SIZE * (head_dim // 2) + t * (head_dim // 16) + u
+    elif side == "v":
+        code_at = ((t // 4 * (head_dim // 8) + c // 4) * 4 + t % 4) * 4 + c % 4
+        scale_at = PAGE_SIZE * (head_dim // 2) + (t // 4 * (head_dim // 16) + u) * 4 + t % 4
+    else:
+        raise ValueError(side)
+    byte = np.take_along_axis(raw, code_at, axis=-1)
     nib = np.where(d % 2 == 0, byte & 0xF, byte >> 4)
-    scl = np.take_along_axis(raw, PAGE_SIZE * (head_dim // 2) + t * (head_dim // 16) + d // 16, axis=-1)
+    scl = np.take_along_axis(raw, scale_at, axis=-1)
     return e2m1_value(nib) * fp8_e4m3fn_value(scl) * global_scale
 
 
@@ -283,7 +299,7 @@ class PagedKVCache:
             raw = self.k_pages[pages[:, None], heads[None, :]]        # [n, Hkv, 9D]
             g = self.k_scale if side == "k" else self.v_scale
             tok = np.broadcast_to(slots[:, None], raw.shape[:2])
-            return nvfp4_token_values(raw, tok, self.head_dim, g)
+            return nvfp4_token_values(raw, tok, self.head_dim, g, side)
         if side == "k":
             raw, scale = self.k_pages[pages, :, slots, :], self.k_scale
         else:

@@ -33,7 +33,7 @@ import torch
 
 __all__ = [
     "Workload", "CONFIGS", "make_workload", "make_query", "make_kv_cache",
-    "encode_fp8_e4m3fn", "encode_nvfp4_rows", "NAN_BYTE",
+    "encode_fp8_e4m3fn", "encode_nvfp4_rows", "arrange_nvfp4_slot", "NAN_BYTE",
     "written_blocks",
 ]
 
@@ -226,6 +226,23 @@ def encode_nvfp4_rows(x, global_scale):
     return packed, s_code.view(torch.uint8)
 
 
+def arrange_nvfp4_slot(codes, scales, v_side):
+    """Bytes of NVFP4 slots from per-token codes [..., 16, D/2] and scales [..., 16, D/16].
+
+    K slots are token-major: the 16 tokens' code bytes, then their scale
+    bytes.  V slots group the tokens by 4 so that a decode lane finds the
+    8-element code units of 4 tokens, and their 4 scales, adjacent: codes as
+    [4 token groups][D/8 units of 4 bytes][4 tokens][4 bytes], then scales as
+    [4 token groups][D/16 scale groups][4 tokens].
+    """
+    *lead, T, half = codes.shape
+    D = 2 * half
+    if v_side:
+        codes = codes.reshape(*lead, T // 4, 4, D // 8, 4).transpose(-3, -2)
+        scales = scales.reshape(*lead, T // 4, 4, D // 16).transpose(-2, -1)
+    return torch.cat([codes.reshape(*lead, -1), scales.reshape(*lead, -1)], dim=-1)
+
+
 def _f32(x):
     """Round a python float to the nearest fp32 value (scales are fp32 scalars)."""
     return float(np.float32(x))
@@ -240,7 +257,8 @@ def make_kv_cache(wl, device="cpu"):
     [pages, Hkv, 16, D] (or one buffer holding both sides when
     block_page_stride is 16: K at 16b + j, V at 16b + 8 + j).  NVFP4: one
     buffer [pages, 2 * Hkv, 9 * D] (slot 2g = K, 2g + 1 = V; per slot the
-    16 tokens' packed codes, then their scales).
+    16 tokens' packed codes, then their scales, arranged by
+    arrange_nvfp4_slot).
     """
     Hkv, D = wl.num_kv_heads, wl.head_dim
     stride = wl.block_page_stride
@@ -297,15 +315,15 @@ def make_kv_cache(wl, device="cpu"):
         slot_bytes = PAGE * (D // 2) + PAGE * (D // 16)
         page_bytes = 2 * Hkv * slot_bytes
 
-        def slots(dat, scl):
+        def slots(dat, scl, v_side):
             dat = torch.where(pm, dat, torch.full_like(dat, NAN_BYTE))
             scl = torch.where(pm, scl, torch.full_like(scl, NAN_BYTE))
-            # [nb, 128, Hkv, *] -> [nb, 8, Hkv, 16 * *]
-            dat = dat.reshape(nb, PAGES_PER_BLOCK, PAGE, Hkv, D // 2).permute(0, 1, 3, 2, 4).reshape(nb, PAGES_PER_BLOCK, Hkv, -1)
-            scl = scl.reshape(nb, PAGES_PER_BLOCK, PAGE, Hkv, D // 16).permute(0, 1, 3, 2, 4).reshape(nb, PAGES_PER_BLOCK, Hkv, -1)
-            return torch.cat([dat, scl], dim=-1)          # [nb, 8, Hkv, slot_bytes]
+            # [nb, 128, Hkv, *] -> [nb, 8 pages, Hkv, 16 tokens, *]
+            dat = dat.reshape(nb, PAGES_PER_BLOCK, PAGE, Hkv, D // 2).permute(0, 1, 3, 2, 4)
+            scl = scl.reshape(nb, PAGES_PER_BLOCK, PAGE, Hkv, D // 16).permute(0, 1, 3, 2, 4)
+            return arrange_nvfp4_slot(dat, scl, v_side)   # [nb, 8, Hkv, slot_bytes]
 
-        both = torch.stack([slots(kd, ks), slots(vd, vs)], dim=3)  # [nb, 8, Hkv, 2, slot]
+        both = torch.stack([slots(kd, ks, False), slots(vd, vs, True)], dim=3)  # [nb, 8, Hkv, 2, slot]
         j = torch.arange(PAGES_PER_BLOCK, device=device)
         kidx = (phys[:, None] * stride + j[None, :]).reshape(-1)
         k_pages = torch.full((num_pages, page_bytes), NAN_BYTE, dtype=torch.uint8, device=device)

@@ -7,10 +7,11 @@ rounding bound.
 """
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
-from synth import encode_nvfp4_rows
+from synth import arrange_nvfp4_slot, encode_nvfp4_rows
 
 # OCP Microscaling Formats v1.0, FP4 E2M1: codes 0..7 are these magnitudes,
 # codes 8..15 their negatives.
@@ -67,6 +68,26 @@ def test_nvfp4_byte_layout():
     nz = np.argwhere(vals != 0)
     assert nz.tolist() == [[5, 74], [5, 75]]
     assert vals[5, 74] == -1.0 * 2.0 * 0.5 and vals[5, 75] == 1.5 * 2.0 * 0.5
+
+
+@pytest.mark.parametrize("side", ["k", "v"])
+def test_nvfp4_slot_order_matches_the_generator(side):
+    # The oracle reads slots by index arithmetic; the generator writes them by
+    # tensor reshapes and transposes.  Random codes and scales, arranged by the
+    # generator, must decode to e2m1(code) * scale read from the unarranged
+    # per-token arrays.
+    g = torch.Generator().manual_seed(11)
+    codes = torch.randint(0, 256, (3, 16, 64), generator=g, dtype=torch.uint8)
+    scales = torch.randint(0, 127, (3, 16, 8), generator=g, dtype=torch.uint8)   # finite E4M3FN
+    slots = arrange_nvfp4_slot(codes, scales, side == "v").numpy()
+    assert slots.shape == (3, 9 * 128)
+    d = np.arange(128)
+    for s in range(3):
+        got = oracle.nvfp4_token_values(np.stack([slots[s]] * 16), np.arange(16), 128, 0.25, side)
+        c = codes[s].numpy()[:, d // 2].astype(np.int64)
+        nib = np.where(d % 2 == 0, c & 0xF, c >> 4)
+        sc = oracle.fp8_e4m3fn_value(scales[s].numpy()[:, d // 16].astype(np.int64))
+        assert np.array_equal(got, oracle.e2m1_value(nib) * sc * 0.25)
 
 
 def test_nvfp4_encode_decode_within_rounding_bound():
