@@ -75,10 +75,16 @@ typedef enum msa_dtype {
  *   16b+8..16b+15 of v_pages (usually the same buffer).
  * kv_dtype MSA_NVFP4 (head_dim 128): one buffer k_pages of pages
  *   [page][2 * num_kv_heads slots][9 * head_dim bytes]; slot 2g is K and
- *   slot 2g+1 is V of kv head g; v_pages is ignored.  Inside a slot, bytes
- *   [0, 8*head_dim) hold token t's e2m1 codes at t*head_dim/2 + d/2 (low
- *   nibble = even d); bytes [8*head_dim, 9*head_dim) hold token t's E4M3FN
- *   scale of elements 16u..16u+15 at 8*head_dim + t*head_dim/16 + u.
+ *   slot 2g+1 is V of kv head g; v_pages is ignored.  A slot holds 16
+ *   tokens: 1024 bytes of e2m1 codes (code byte c of a token holds elements
+ *   2c, low nibble, and 2c+1), then 128 E4M3FN scale bytes (scale u covers
+ *   elements 16u..16u+15).
+ *     K slot, token-major: code byte c of token t at t*64 + c; scale u at
+ *       1024 + t*8 + u.
+ *     V slot, tokens in groups of 4: code byte c of token t at
+ *       ((t/4*16 + c/4)*4 + t%4)*4 + c%4; scale u at 1024 + (t/4*8 + u)*4 + t%4
+ *       (the decode reads one token group's 8 elements and their 4 scales
+ *       with one load each).
  *
  * k_scale / v_scale: device fp32 scalars (NULL = 1.0).  fp8: the
  *   per-tensor dequant multipliers; NVFP4: the per-tensor global scales.
