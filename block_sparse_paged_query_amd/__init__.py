@@ -27,7 +27,7 @@ import torch
 __all__ = [
     "MsaError", "KVCache", "library_path", "load_library",
     "msa_build_sparse_block_table", "msa_query_token_positions",
-    "msa_sparse_decode", "msa_sparse_prefill", "msa_insert_index_cache",
+    "msa_sparse_decode", "msa_sparse_prefill", "msa_sparse_attention", "msa_insert_index_cache",
     "msa_debug_dequant_tokens", "msa_decode_workspace_size",
     "MSA_BF16", "MSA_FP16", "MSA_FP8_E4M3FN", "MSA_NVFP4", "MSA_FP32",
 ]
@@ -70,6 +70,8 @@ _SIGS = {
     "msa_prefill_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_prefill": ([_P, _I32, _I32, _I32, ctypes.POINTER(_KV), _P, _I64, _I32, _P, _I64, _I32, _I32,
                             _P, _P, _F32, _P, _P, _SZ, _P], _I32),
+    "msa_sparse_attention": ([_P, _I32, _I32, _I32, ctypes.POINTER(_KV), _P, _I64, _I32, _I32, _I32,
+                              _P, _I64, _I32, _P, _I32, _P, _I64, _I32, _P, _P, _F32, _P, _P, _SZ, _P], _I32),
     "msa_insert_index_cache": ([_P, _I64, _I64, _I32, _I32, _I32, _P, _I64, _I64, _I64, _I32, _I32, _P, _I64,
                                 _P], _I32),
     "msa_debug_dequant_tokens": ([ctypes.POINTER(_KV), _P, _P, _I32, _P, _P, _P], _I32),
@@ -276,6 +278,65 @@ def msa_sparse_prefill(q, kv: KVCache, topk, block_table, cu_seqlens_q, seq_lens
           topk.shape[1], _ptr(block_table), block_table.stride(0), block_table.shape[1], seq_lens.shape[0],
           _ptr(cu_seqlens_q), _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(dev))
+    return out
+
+
+def msa_sparse_attention(q, kv: KVCache, topk, num_decode_tokens, softmax_scale, *, decode_block_table=None,
+                         decode_seq_lens=None, decode_query_len=1, prefill_block_table=None,
+                         prefill_cu_seqlens_q=None, prefill_seq_lens=None, out=None, workspace=None):
+    """A whole batch: decode rows [0, num_decode_tokens), then prefill rows.
+
+    q/out [num_tokens, Hq, D] bf16; topk [num_tokens, k] token-major.  The
+    decode part uses decode_block_table / decode_seq_lens, the prefill part
+    prefill_block_table / prefill_cu_seqlens_q (from the first prefill row) /
+    prefill_seq_lens; a part with no rows needs none of its tensors.
+    """
+    if topk.dim() == 3:
+        topk = topk[0]
+    dev = q.device
+    _check_q(q)
+    _need(topk, "topk", torch.int32, 2, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_q(out, "out")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    num_tokens, hq, d = q.shape
+    if topk.shape[0] != num_tokens:
+        raise ValueError(f"topk has {topk.shape[0]} rows, q has {num_tokens}")
+    if d != kv.head_dim:
+        raise ValueError(f"q head_dim {d} != cache head_dim {kv.head_dim}")
+    nd = int(num_decode_tokens)
+    if not 0 <= nd <= num_tokens:
+        raise ValueError(f"num_decode_tokens {nd} of {num_tokens} rows")
+    dbt = dsl = pbt = pcu = psl = None
+    if nd > 0:
+        _need(decode_block_table, "decode_block_table", torch.int32, 2, dev)
+        _need(decode_seq_lens, "decode_seq_lens", torch.int32, 1, dev)
+        if nd != decode_seq_lens.shape[0] * decode_query_len:
+            raise ValueError(f"{nd} decode rows; {decode_seq_lens.shape[0]} requests x decode_query_len "
+                             f"{decode_query_len}")
+        dbt, dsl = decode_block_table, decode_seq_lens
+    if nd < num_tokens:
+        _need(prefill_block_table, "prefill_block_table", torch.int32, 2, dev)
+        _need(prefill_cu_seqlens_q, "prefill_cu_seqlens_q", torch.int32, 1, dev)
+        _need(prefill_seq_lens, "prefill_seq_lens", torch.int32, 1, dev)
+        if prefill_cu_seqlens_q.shape[0] != prefill_seq_lens.shape[0] + 1:
+            raise ValueError("prefill_cu_seqlens_q must have num_prefill_reqs + 1 entries")
+        pbt, pcu, psl = prefill_block_table, prefill_cu_seqlens_q, prefill_seq_lens
+    if workspace is None:
+        nbytes = msa_decode_workspace_size(max(nd, 1), hq, d, topk.shape[1])
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    kvs = kv._struct()
+    _call("msa_sparse_attention", _ptr(q), MSA_BF16, num_tokens, hq, ctypes.byref(kvs), _ptr(topk), topk.stride(0),
+          topk.shape[1], nd, decode_query_len,
+          None if dbt is None else _ptr(dbt), 0 if dbt is None else dbt.stride(0), 0 if dbt is None else dbt.shape[1],
+          None if dsl is None else _ptr(dsl),
+          0 if psl is None else psl.shape[0],
+          None if pbt is None else _ptr(pbt), 0 if pbt is None else pbt.stride(0), 0 if pbt is None else pbt.shape[1],
+          None if pcu is None else _ptr(pcu), None if psl is None else _ptr(psl),
+          float(softmax_scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _stream(dev))
     return out
 
 

@@ -225,12 +225,13 @@ MSA_API size_t msa_decode_workspace_size(int32_t total_q, int32_t num_q_heads, i
   return split_bytes(total_q, num_q_heads, head_dim, max_ns);
 }
 
-MSA_API msa_status_t msa_sparse_decode(const void* q, int32_t q_dtype, int32_t num_reqs, int32_t decode_query_len,
-                                       int32_t num_q_heads, const msa_kv_cache_t* kv, const int32_t* topk,
-                                       int64_t topk_row_stride, int32_t topk_k, const int32_t* block_table,
-                                       int64_t bt_row_stride, int32_t bt_cols, const int32_t* seq_lens,
-                                       float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                                       hipStream_t stream) {
+// Decode: validate every host-visible argument, then (if `launch`) enqueue.
+static msa_status_t decode_impl(bool launch, const void* q, int32_t q_dtype, int32_t num_reqs,
+                                int32_t decode_query_len, int32_t num_q_heads, const msa_kv_cache_t* kv,
+                                const int32_t* topk, int64_t topk_row_stride, int32_t topk_k,
+                                const int32_t* block_table, int64_t bt_row_stride, int32_t bt_cols,
+                                const int32_t* seq_lens, float softmax_scale, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   MSA_CHECK(num_reqs >= 0 && decode_query_len >= 1, MSA_ERR_INVALID_ARGUMENT, "num_reqs %d, decode_query_len %d",
             num_reqs, decode_query_len);
   const int64_t rows64 = (int64_t)num_reqs * decode_query_len;
@@ -241,6 +242,7 @@ MSA_API msa_status_t msa_sparse_decode(const void* q, int32_t q_dtype, int32_t n
   if (st != MSA_OK) return st;
   if (rows == 0) return ok();
   MSA_CHECK(seq_lens != nullptr, MSA_ERR_INVALID_ARGUMENT, "seq_lens is NULL");
+  if (!launch) return ok();
   msa::AttendArgs a = attend_args(q, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table, bt_row_stride,
                                   bt_cols, softmax_scale, out);
   a.seq_lens = seq_lens;
@@ -259,6 +261,17 @@ MSA_API msa_status_t msa_sparse_decode(const void* q, int32_t q_dtype, int32_t n
                     "decode launch");
 }
 
+MSA_API msa_status_t msa_sparse_decode(const void* q, int32_t q_dtype, int32_t num_reqs, int32_t decode_query_len,
+                                       int32_t num_q_heads, const msa_kv_cache_t* kv, const int32_t* topk,
+                                       int64_t topk_row_stride, int32_t topk_k, const int32_t* block_table,
+                                       int64_t bt_row_stride, int32_t bt_cols, const int32_t* seq_lens,
+                                       float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  return decode_impl(true, q, q_dtype, num_reqs, decode_query_len, num_q_heads, kv, topk, topk_row_stride, topk_k,
+                     block_table, bt_row_stride, bt_cols, seq_lens, softmax_scale, out, workspace, workspace_bytes,
+                     stream);
+}
+
 MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim, int32_t topk_k) {
   (void)total_q;
   (void)num_q_heads;
@@ -267,14 +280,12 @@ MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, 
   return 0;
 }
 
-MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,
-                                        const msa_kv_cache_t* kv, const int32_t* topk, int64_t topk_row_stride,
-                                        int32_t topk_k, const int32_t* block_table, int64_t bt_row_stride,
-                                        int32_t bt_cols, int32_t num_reqs, const int32_t* cu_seqlens_q,
-                                        const int32_t* seq_lens, float softmax_scale, void* out, void* workspace,
-                                        size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+// Prefill: validate every host-visible argument, then (if `launch`) enqueue.
+static msa_status_t prefill_impl(bool launch, const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,
+                                 const msa_kv_cache_t* kv, const int32_t* topk, int64_t topk_row_stride,
+                                 int32_t topk_k, const int32_t* block_table, int64_t bt_row_stride, int32_t bt_cols,
+                                 int32_t num_reqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                 float softmax_scale, void* out, hipStream_t stream) {
   MSA_CHECK(total_q >= 0 && num_reqs >= 0, MSA_ERR_INVALID_ARGUMENT, "negative total_q %d or num_reqs %d", total_q,
             num_reqs);
   MSA_CHECK(total_q <= (1 << 24), MSA_ERR_UNSUPPORTED, "%d prefill rows: at most 2^24", total_q);
@@ -284,6 +295,7 @@ MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t 
   if (total_q == 0) return ok();
   MSA_CHECK(num_reqs >= 1 && cu_seqlens_q && seq_lens, MSA_ERR_INVALID_ARGUMENT,
             "prefill needs num_reqs >= 1, cu_seqlens_q and seq_lens");
+  if (!launch) return ok();
   msa::AttendArgs a = attend_args(q, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table, bt_row_stride,
                                   bt_cols, softmax_scale, out);
   a.seq_lens = seq_lens;
@@ -295,6 +307,56 @@ MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t 
     return hip_status(msa::launch_prefill_blocks(a, fmt_of(kv->kv_dtype), stream), "prefill launch");
   return hip_status(msa::launch_attend_rows(a, fmt_of(kv->kv_dtype), msa::kModePrefill, total_q, stream),
                     "prefill launch");
+}
+
+MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,
+                                        const msa_kv_cache_t* kv, const int32_t* topk, int64_t topk_row_stride,
+                                        int32_t topk_k, const int32_t* block_table, int64_t bt_row_stride,
+                                        int32_t bt_cols, int32_t num_reqs, const int32_t* cu_seqlens_q,
+                                        const int32_t* seq_lens, float softmax_scale, void* out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return prefill_impl(true, q, q_dtype, total_q, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table,
+                      bt_row_stride, bt_cols, num_reqs, cu_seqlens_q, seq_lens, softmax_scale, out, stream);
+}
+
+MSA_API msa_status_t msa_sparse_attention(
+    const void* q, int32_t q_dtype, int32_t num_tokens, int32_t num_q_heads, const msa_kv_cache_t* kv,
+    const int32_t* topk, int64_t topk_row_stride, int32_t topk_k, int32_t num_decode_tokens,
+    int32_t decode_query_len, const int32_t* decode_block_table, int64_t decode_bt_row_stride,
+    int32_t decode_bt_cols, const int32_t* decode_seq_lens, int32_t num_prefill_reqs,
+    const int32_t* prefill_block_table, int64_t prefill_bt_row_stride, int32_t prefill_bt_cols,
+    const int32_t* prefill_cu_seqlens_q, const int32_t* prefill_seq_lens, float softmax_scale, void* out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MSA_CHECK(kv != nullptr, MSA_ERR_INVALID_ARGUMENT, "kv cache descriptor is NULL");
+  MSA_CHECK(num_tokens >= 0 && num_decode_tokens >= 0 && num_decode_tokens <= num_tokens, MSA_ERR_INVALID_ARGUMENT,
+            "num_decode_tokens %d of num_tokens %d", num_decode_tokens, num_tokens);
+  MSA_CHECK(decode_query_len >= 1 && num_decode_tokens % decode_query_len == 0, MSA_ERR_INVALID_ARGUMENT,
+            "num_decode_tokens %d is not a multiple of decode_query_len %d", num_decode_tokens, decode_query_len);
+  MSA_CHECK(num_q_heads >= 1 && kv->head_dim >= 1, MSA_ERR_INVALID_ARGUMENT, "num_q_heads %d, head_dim %d",
+            num_q_heads, kv->head_dim);
+  const int32_t nd = num_decode_tokens, np = num_tokens - num_decode_tokens;
+  const int64_t row_bytes = (int64_t)num_q_heads * kv->head_dim * 2;   // bf16 q / out rows
+  const uint8_t* qp = q ? static_cast<const uint8_t*>(q) + (int64_t)nd * row_bytes : nullptr;
+  uint8_t* op = out ? static_cast<uint8_t*>(out) + (int64_t)nd * row_bytes : nullptr;
+  const int32_t* tp = topk ? topk + (int64_t)nd * topk_row_stride : nullptr;
+  // validate both parts before enqueuing either
+  msa_status_t st = decode_impl(false, q, q_dtype, nd / decode_query_len, decode_query_len, num_q_heads, kv, topk,
+                                topk_row_stride, topk_k, decode_block_table, decode_bt_row_stride, decode_bt_cols,
+                                decode_seq_lens, softmax_scale, out, workspace, workspace_bytes, stream);
+  if (st != MSA_OK) return st;
+  st = prefill_impl(false, qp, q_dtype, np, num_q_heads, kv, tp, topk_row_stride, topk_k, prefill_block_table,
+                    prefill_bt_row_stride, prefill_bt_cols, num_prefill_reqs, prefill_cu_seqlens_q, prefill_seq_lens,
+                    softmax_scale, op, stream);
+  if (st != MSA_OK) return st;
+  st = decode_impl(true, q, q_dtype, nd / decode_query_len, decode_query_len, num_q_heads, kv, topk, topk_row_stride,
+                   topk_k, decode_block_table, decode_bt_row_stride, decode_bt_cols, decode_seq_lens, softmax_scale,
+                   out, workspace, workspace_bytes, stream);
+  if (st != MSA_OK) return st;
+  return prefill_impl(true, qp, q_dtype, np, num_q_heads, kv, tp, topk_row_stride, topk_k, prefill_block_table,
+                      prefill_bt_row_stride, prefill_bt_cols, num_prefill_reqs, prefill_cu_seqlens_q,
+                      prefill_seq_lens, softmax_scale, op, stream);
 }
 
 MSA_API msa_status_t msa_insert_index_cache(const void* index_k, int64_t k_stride0, int64_t k_stride1, int32_t n,

@@ -225,6 +225,35 @@ MSA_API msa_status_t msa_sparse_prefill(
     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * One layer's whole batch in one call: decode rows first, then prefill rows.
+ * [FI] MiniMaxM3SparseFlashInferImpl.forward: the first num_decode_tokens
+ * tokens are the decode tokens (their requests, block table and lengths),
+ * the rest are prefill tokens (cu_seqlens_q, block table and lengths of the
+ * prefill requests); the top-k rows are token-major over the whole batch.
+ *
+ * q, out [num_tokens][num_q_heads][head_dim] bf16, contiguous; topk
+ * [num_tokens][topk_row_stride].  Rows [0, num_decode_tokens) go through
+ * msa_sparse_decode (num_decode_tokens / decode_query_len requests), rows
+ * [num_decode_tokens, num_tokens) through msa_sparse_prefill with
+ * prefill_cu_seqlens_q counted from the first prefill row; either part may
+ * be empty.  Both parts are validated before anything is enqueued; then
+ * they run in that order on `stream`, with no host synchronisation (the call
+ * can be captured into a HIP graph).  workspace as for msa_sparse_decode.
+ */
+MSA_API msa_status_t msa_sparse_attention(
+    const void* q, int32_t q_dtype, int32_t num_tokens, int32_t num_q_heads,
+    const msa_kv_cache_t* kv,
+    const int32_t* topk, int64_t topk_row_stride, int32_t topk_k,
+    int32_t num_decode_tokens, int32_t decode_query_len,
+    const int32_t* decode_block_table, int64_t decode_bt_row_stride, int32_t decode_bt_cols,
+    const int32_t* decode_seq_lens,
+    int32_t num_prefill_reqs,
+    const int32_t* prefill_block_table, int64_t prefill_bt_row_stride, int32_t prefill_bt_cols,
+    const int32_t* prefill_cu_seqlens_q, const int32_t* prefill_seq_lens,
+    float softmax_scale, void* out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Scatter index keys into the key-only side cache.
  * [SPA] minimax_m3_insert_index_cache: keys [N, D] into a cache [B, T, D]
  * through a length-N slot mapping; empty input returns at once; the cache's

@@ -120,6 +120,25 @@ def test_prefill_rejects_unsupported_shapes():
     assert d96 == 2
 
 
+def _mixed(kv, **kw):
+    args = dict(q=FAKE, q_dtype=0, num_tokens=10, hq=64, kv=ctypes.byref(kv), topk=FAKE, topk_stride=16, topk_k=16,
+                nd=4, dql=2, dbt=FAKE, dbt_stride=64, dbt_cols=64, dsl=FAKE, npre=1, pbt=FAKE, pbt_stride=64,
+                pbt_cols=64, pcu=FAKE, psl=FAKE, scale=0.1, out=FAKE, ws=None, ws_bytes=0)
+    args.update(kw)
+    return _lib().msa_sparse_attention(*args.values(), None)
+
+
+def test_mixed_batch_validates_both_parts_first():
+    # every check runs before any HIP call, so fake device pointers are safe
+    kv = _kv()
+    assert _mixed(kv, nd=11) == 1                 # more decode rows than rows
+    assert _mixed(kv, nd=3) == 1                  # not a multiple of decode_query_len
+    assert _mixed(kv, dsl=None) == 1              # decode part without seq_lens
+    assert _mixed(kv, pcu=None) == 1              # prefill part without cu_seqlens_q
+    assert _mixed(kv, q_dtype=1) == 2             # fp16 queries are not served
+    assert _mixed(kv, num_tokens=0, nd=0) == 0    # empty batch: nothing to do
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(msa, "_lib", None)
     monkeypatch.setattr(msa, "library_path", lambda: str(tmp_path / "libmsa.so"))

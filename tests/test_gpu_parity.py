@@ -213,6 +213,78 @@ def test_prefill_parity_full_size_sampled(kv_dtype):
     _parity(wl, rows)
 
 
+def _block_outer(cache, layers=3, layer=1):
+    """The same pages re-homed in a block-outer buffer of `layers` layers:
+    page p of this layer at (p * layers + layer) * page bytes, the other
+    layers' pages NaN-filled."""
+    out = dict(cache)
+    for key in ("k_pages", "v_pages"):
+        t = cache[key]
+        if t is None:
+            continue
+        n, pb = t.shape[0], t[0].numel() * t.element_size()
+        big = torch.full((n, layers, pb), 0xFF, dtype=torch.uint8, device=t.device)
+        big[:, layer] = t.reshape(n, -1).view(torch.uint8)
+        out[key] = big[:, layer].view(t.shape)       # page stride = layers * page bytes
+    return out
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("C2s", {}), ("C3s", {}), ("C5s", {}),
+    ("C4s", {}), ("C4s", dict(kv_dtype="fp8")), ("C4s", dict(kv_dtype="nvfp4")),
+])
+def test_block_outer_page_stride(name, kw):
+    # [NV4] supported_kv_cache_layouts: the kernels take the page stride from
+    # the cache (stride(0)) and address pages in 64 bits, so block-outer
+    # packing (one buffer, every layer's copy of a page adjacent) works too.
+    # Identical outputs to the same cache laid out densely.
+    wl = make_workload(name, **kw)
+    cache = make_kv_cache(wl, DEV)
+    q = make_query(wl, DEV)
+    dense = _run(wl, cache, q)
+    outer = _block_outer(cache)
+    assert _kv(wl, outer)._struct().page_stride_bytes == 3 * _kv(wl, cache)._struct().page_stride_bytes
+    got = _run(wl, outer, q)
+    assert torch.equal(dense, got)
+
+
+@pytest.mark.parametrize("dql", [1, 2])
+def test_mixed_batch_matches_separate_calls(dql):
+    # [FI] forward: decode tokens first, then prefill tokens, one cache, one
+    # token-major top-k buffer.  A decode workload and a prefill workload share
+    # one cache (the prefill's blocks placed after the decode's); the single
+    # call must equal the two separate calls row for row, and each part is
+    # checked against the oracle.
+    dec = make_workload("C2s", dql=dql, seed=61)
+    pre = make_workload("C4s", seed=62)
+    cd, cp = make_kv_cache(dec, DEV), make_kv_cache(pre, DEV)
+    shared = dict(cd)
+    shared["k_pages"] = torch.cat([cd["k_pages"], cp["k_pages"]])
+    shared["v_pages"] = torch.cat([cd["v_pages"], cp["v_pages"]])
+    kv = _kv(dec, shared)
+    qd, qp = make_query(dec, DEV), make_query(pre, DEV)
+    pre_bt = pre.block_table + dec.num_phys_blocks
+    q = torch.cat([qd, qp])
+    topk = _dev(np.concatenate([dec.topk, pre.topk]))
+    nd = dec.total_q
+    out = msa.msa_sparse_attention(q, kv, topk, nd, dec.softmax_scale,
+                                   decode_block_table=_dev(dec.block_table), decode_seq_lens=_dev(dec.seq_lens),
+                                   decode_query_len=dql, prefill_block_table=_dev(pre_bt),
+                                   prefill_cu_seqlens_q=_dev(pre.cu_seqlens_q), prefill_seq_lens=_dev(pre.seq_lens))
+    want_d = msa.msa_sparse_decode(qd, kv, topk[:nd], _dev(dec.block_table), _dev(dec.seq_lens), dec.softmax_scale,
+                                   decode_query_len=dql)
+    want_p = msa.msa_sparse_prefill(qp, kv, topk[nd:], _dev(pre_bt), _dev(pre.cu_seqlens_q), _dev(pre.seq_lens),
+                                    pre.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:nd], want_d) and torch.equal(out[nd:], want_p)
+    for wl, got, qq, cache in ((dec, want_d, qd, cd), (pre, want_p, qp, cp)):
+        req, pos = oracle_positions(wl)
+        rows = np.arange(wl.total_q)
+        oc, bt, _, _ = compact_oracle_inputs(wl, cache, rows)
+        want = oracle.sparse_attention(q_f64(qq), oc, wl.topk, bt, req, pos, wl.softmax_scale, rows=rows)
+        assert np.abs(got.float().cpu().numpy() - want).max() <= ATOL
+
+
 def test_decode_deterministic():
     wl = make_workload("C3s")
     cache = make_kv_cache(wl, DEV)
