@@ -285,6 +285,43 @@ def test_mixed_batch_matches_separate_calls(dql):
         assert np.abs(got.float().cpu().numpy() - want).max() <= ATOL
 
 
+def test_mixed_batch_in_a_graph():
+    # The whole-batch call enqueues kernels only (no host sync, no memset), so
+    # it can be captured.  Replays, with eager work and synchronisations in
+    # between, must each equal the eager result.
+    dec = make_workload("C2s", seed=71)
+    pre = make_workload("C4s", seed=72)
+    cd, cp = make_kv_cache(dec, DEV), make_kv_cache(pre, DEV)
+    shared = dict(cd)
+    shared["k_pages"] = torch.cat([cd["k_pages"], cp["k_pages"]])
+    shared["v_pages"] = torch.cat([cd["v_pages"], cp["v_pages"]])
+    kv = _kv(dec, shared)
+    q = torch.cat([make_query(dec, DEV), make_query(pre, DEV)])
+    topk = _dev(np.concatenate([dec.topk, pre.topk]))
+    args = dict(decode_block_table=_dev(dec.block_table), decode_seq_lens=_dev(dec.seq_lens),
+                prefill_block_table=_dev(pre.block_table + dec.num_phys_blocks),
+                prefill_cu_seqlens_q=_dev(pre.cu_seqlens_q), prefill_seq_lens=_dev(pre.seq_lens))
+    ws = torch.empty(msa.msa_decode_workspace_size(dec.total_q, 64, 128, 16), dtype=torch.uint8, device=DEV)
+    eager = msa.msa_sparse_attention(q, kv, topk, dec.total_q, dec.softmax_scale, workspace=ws, **args)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture, on the capture stream
+        msa.msa_sparse_attention(q, kv, topk, dec.total_q, dec.softmax_scale, out=out, workspace=ws, **args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        msa.msa_sparse_attention(q, kv, topk, dec.total_q, dec.softmax_scale, out=out, workspace=ws, **args)
+    for i in range(4):
+        out.fill_(float("nan"))              # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+
+
 def test_decode_deterministic():
     wl = make_workload("C3s")
     cache = make_kv_cache(wl, DEV)
