@@ -47,13 +47,16 @@ DESCR = {
 
 def workload_key(args):
     """Config name, with the page format when --kv-dtype overrides it."""
-    return args.config + (f"/{args.kv_dtype}" if args.kv_dtype else "")
+    return (args.config + (f"/{args.kv_dtype}" if args.kv_dtype else "")
+            + ("/rows128" if args.layout == "rows128" else ""))
 
 
 def describe(args):
     d = DESCR[args.config]
     if args.kv_dtype:
         d = d.replace("bf16", args.kv_dtype).replace("fp8 e4m3", args.kv_dtype).replace("NVFP4", args.kv_dtype)
+    if args.layout == "rows128":
+        d += ", 128-token pages with K|V-interleaved rows"
     return d
 
 
@@ -196,6 +199,8 @@ def main():
     ap.add_argument("--config", default="C2", choices=sorted(DESCR))
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8", "nvfp4"], default=None,
                     help="page format instead of the workload's own (fp8 / NVFP4 prefill)")
+    ap.add_argument("--layout", choices=["page16", "rows128"], default="page16",
+                    help="cache layout (rows128: bf16 / fp8 only)")
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -223,7 +228,7 @@ def main():
     import torch
 
     import block_sparse_paged_query_amd as msa
-    from synth import make_kv_cache, make_query, make_workload
+    from synth import make_kv_cache, make_query, make_workload, rows128_cache
 
     dev = "cuda"
     if args.copy_probe:
@@ -238,6 +243,8 @@ def main():
     wl = make_workload(args.config, **({"kv_dtype": args.kv_dtype} if args.kv_dtype else {}))
     print(f"[bench] {workload_key(args)}: building inputs", file=sys.stderr, flush=True)
     cache = make_kv_cache(wl, dev)
+    if args.layout == "rows128":
+        cache = rows128_cache(cache, wl)
     q = make_query(wl, dev)
     topk = torch.from_numpy(wl.topk).to(dev)
     bt = torch.from_numpy(wl.block_table).to(dev)
@@ -253,7 +260,8 @@ def main():
         vp = cache["v_pages"]
         if vp is not None and i > 0:
             vp = vp.clone()
-        layers.append(msa.KVCache(wl.kv_dtype, kp, vp, wl.num_kv_heads, wl.head_dim, wl.block_page_stride, ks, vs))
+        layers.append(msa.KVCache(wl.kv_dtype, kp, vp, wl.num_kv_heads, wl.head_dim, wl.block_page_stride, ks, vs,
+                                  layout=cache["layout"]))
     out = torch.empty_like(q)
 
     # work of one step, from the library's own context lengths

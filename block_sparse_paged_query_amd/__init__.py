@@ -36,6 +36,7 @@ MSA_BF16, MSA_FP16, MSA_FP8_E4M3FN, MSA_NVFP4, MSA_FP32 = 0, 1, 2, 3, 4
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARGUMENT", 2: "MSA_ERR_UNSUPPORTED",
            3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP"}
 _KV_DTYPES = {"bf16": MSA_BF16, "fp8": MSA_FP8_E4M3FN, "nvfp4": MSA_NVFP4}
+_KV_LAYOUTS = {"page16": 0, "rows128": 1}
 
 
 class MsaError(RuntimeError):
@@ -55,6 +56,7 @@ class _KV(ctypes.Structure):
         ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
         ("page_stride_bytes", ctypes.c_int64), ("num_pages", ctypes.c_int64),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("kv_layout", ctypes.c_int32),
     ]
 
 
@@ -129,7 +131,10 @@ class KVCache:
 
     ``k_pages`` / ``v_pages``: tensors whose first dimension is the page (any
     dtype; bytes are what count).  ``k_scale`` / ``v_scale``: 1-element fp32
-    device tensors or None (= 1.0).
+    device tensors or None (= 1.0).  ``layout``: "page16" (16-token pages, K
+    and V planes or NVFP4 slots) or "rows128" (128-token pages
+    [pages, Hkv, 128, 2 * D] with K|V-interleaved rows; ``v_pages`` None or
+    the V view ``cache[..., D:]`` of the same tensor).
     """
     kv_dtype: str
     k_pages: torch.Tensor
@@ -139,10 +144,13 @@ class KVCache:
     block_page_stride: int = 8
     k_scale: torch.Tensor | None = None
     v_scale: torch.Tensor | None = None
+    layout: str = "page16"
 
     def _struct(self):
         if self.kv_dtype not in _KV_DTYPES:
             raise ValueError(f"kv_dtype {self.kv_dtype!r}: one of {sorted(_KV_DTYPES)}")
+        if self.layout not in _KV_LAYOUTS:
+            raise ValueError(f"layout {self.layout!r}: one of {sorted(_KV_LAYOUTS)}")
         kp = self.k_pages
         for name, s in (("k_scale", self.k_scale), ("v_scale", self.v_scale)):
             if s is not None:
@@ -159,7 +167,8 @@ class KVCache:
                    kp.data_ptr(), None if self.v_pages is None else self.v_pages.data_ptr(),
                    stride, kp.shape[0],
                    None if self.k_scale is None else self.k_scale.data_ptr(),
-                   None if self.v_scale is None else self.v_scale.data_ptr())
+                   None if self.v_scale is None else self.v_scale.data_ptr(),
+                   _KV_LAYOUTS[self.layout])
 
 
 def msa_build_sparse_block_table(topk, block_table, *, seq_lens=None, decode_query_len=1, query_req_id=None,

@@ -138,16 +138,16 @@ __device__ __forceinline__ uint32_t buf_load1(BufRsrc r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, AUX);
 }
 
-// Byte offsets of one lane's loads inside a page tile (bf16 / fp8: the
-// [16][D] tile of one kv head) or inside an NVFP4 slot's code / scale rows.
-// K: token r of each page; V: tokens 4g .. 4g+3 of each page (tau order),
-// columns r*NN .. r*NN + NN.
+// Byte offsets of one lane's loads inside a page tile (bf16 / fp8: the 16
+// token rows of one kv head, `rs` bytes apart) or inside an NVFP4 slot's
+// code / scale rows.  K: token r of each page; V: tokens 4g .. 4g+3 of each
+// page (tau order), columns r*NN .. r*NN + NN.
 struct LaneOffsets {
-  uint32_t k, v, ks, vs;
+  uint32_t k, v, ks, vs, rs;
 };
 
 template <int FMT, int D>
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane, int rs) {
   const int r = lane & 15, g = lane >> 4;
   LaneOffsets o;
   if constexpr (FMT == kFmtNvfp4) {
@@ -155,11 +155,13 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
     o.ks = r * (D / 16) + 2 * g;          // scales of groups 2g and 2g + 1
     o.v = (g * (D / 8) + r) * 16;         // 8 codes (d in [8r, 8r + 8)) of tokens 4g .. 4g+3
     o.vs = (g * (D / 16) + (r >> 1)) * 4; // their scales of group r / 2
+    o.rs = 0;
   } else {
-    constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1, ROW = D * ESZ, NN = D / 16;
-    o.k = r * ROW + 16 * g;
-    o.v = 4 * g * ROW + r * NN * ESZ;
+    constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1, NN = D / 16;
+    o.k = r * rs + 16 * g;
+    o.v = 4 * g * rs + r * NN * ESZ;
     o.ks = o.vs = 0;
+    o.rs = rs;
   }
   return o;
 }
@@ -179,23 +181,17 @@ __device__ __forceinline__ ChunkLoc chunk_loc(const AttendArgs& a, const int* sl
   ChunkLoc L;
   const bool in = c < c_end;
   const int phys = __builtin_amdgcn_readfirstlane(slot_list[in ? (c >> 2) : 0]);
-  const int64_t pg0 = (int64_t)phys * a.block_page_stride + 2 * (c & 3);
+  const int64_t u0 = (int64_t)phys * a.blk_units + 2 * (c & 3);
   // (the 64-bit compares run on the vector unit: take the verdict back to a scalar)
   L.ok = __builtin_amdgcn_readfirstlane(
-      (int)(phys >= 0 && pg0 + 1 < a.num_pages && (FMT == kFmtNvfp4 || pg0 + a.v_page_offset + 1 < a.num_pages)));
+      (int)(phys >= 0 && u0 + 1 < a.num_units && (FMT == kFmtNvfp4 || u0 + a.v_unit_offset + 1 < a.num_units)));
   const int rem = ctx - c * 32;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     L.valid[t] = __builtin_amdgcn_readfirstlane((in && L.ok) ? min(max(rem - 16 * t, 0), kPageTokens) : 0);
-    if constexpr (FMT == kFmtNvfp4) {
-      constexpr int SLOT = 9 * D;
-      L.k[t] = a.k_base + (pg0 + t) * a.page_stride + (int64_t)(2 * kvh) * SLOT;
-      L.v[t] = L.k[t] + SLOT;
-    } else {
-      constexpr int ROW = D * (FMT == kFmtBf16 ? 2 : 1);
-      L.k[t] = a.k_base + (pg0 + t) * a.page_stride + (int64_t)kvh * kPageTokens * ROW;
-      L.v[t] = a.v_base + (pg0 + a.v_page_offset + t) * a.page_stride + (int64_t)kvh * kPageTokens * ROW;
-    }
+    const int64_t off = (u0 + t) * a.sub_stride + (int64_t)kvh * a.head_stride;
+    L.k[t] = a.k_base + off;
+    L.v[t] = a.v_base + off;
   }
   return L;
 }
@@ -230,10 +226,16 @@ __device__ __forceinline__ void issue_loads(ChunkRaw<FMT, D>& raw, const ChunkLo
       raw.vs[t] = buf_load4<AUX>(vsr, o.vs);
     }
   } else {
+    // A descriptor ends with the last valid token's row piece: rows past it
+    // (and, in K|V-interleaved rows, the other side's half) read as 0.
     constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1, ROW = D * ESZ;
+    const int rs = o.rs;
+    int span[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) span[t] = L.valid[t] > 0 ? (L.valid[t] - 1) * rs + ROW : 0;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const BufRsrc kr = make_rsrc(L.k[t], L.valid[t] * ROW);
+      const BufRsrc kr = make_rsrc(L.k[t], span[t]);
       if constexpr (FMT == kFmtBf16) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) raw.k[t][kk] = buf_load16<AUX>(kr, o.k + 64 * kk);
@@ -244,19 +246,19 @@ __device__ __forceinline__ void issue_loads(ChunkRaw<FMT, D>& raw, const ChunkLo
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const BufRsrc vr = make_rsrc(L.v[t], L.valid[t] * ROW);
+      const BufRsrc vr = make_rsrc(L.v[t], span[t]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t* dst = raw.v[4 * t + i];
         constexpr int W = NN * ESZ / 4;   // dwords of one lane's row piece
         if constexpr (W == 4) {
-          const u32x4 x = buf_load16<AUX>(vr, o.v + i * ROW);
+          const u32x4 x = buf_load16<AUX>(vr, o.v + i * rs);
           dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
         } else if constexpr (W == 2) {
-          const u32x2 x = buf_load8<AUX>(vr, o.v + i * ROW);
+          const u32x2 x = buf_load8<AUX>(vr, o.v + i * rs);
           dst[0] = x[0]; dst[1] = x[1];
         } else {
-          dst[0] = buf_load4<AUX>(vr, o.v + i * ROW);
+          dst[0] = buf_load4<AUX>(vr, o.v + i * rs);
         }
       }
     }
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   const int c1 = (int)((int64_t)nchunks * (split + 1) / a.nsplit);
 
   // this wave's chunks: cw, cw + nw, cw + 2 nw, ... below c1; NB of them in flight
-  const LaneOffsets lo = lane_offsets<FMT, D>(lane);
+  const LaneOffsets lo = lane_offsets<FMT, D>(lane, a.row_stride);
   const int cw = c0 + wave;
   const int n_w = cw < c1 ? (c1 - cw + nw - 1) / nw : 0;
   ChunkRaw<FMT, D> raw[NB];

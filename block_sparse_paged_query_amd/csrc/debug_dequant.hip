@@ -13,21 +13,22 @@
 
 namespace msa {
 
-__device__ __forceinline__ void dequant_pair(int fmt, const uint8_t* page_head, bool v_side, int slot, int D, int e,
+// `src`: bf16 / fp8 the token's row, NVFP4 the page's slot of the head.
+__device__ __forceinline__ void dequant_pair(int fmt, const uint8_t* src, bool v_side, int slot, int e,
                                              float* x0, float* x1) {
   if (fmt == kFmtBf16) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(page_head + (slot * D + e) * 2);
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(src + e * 2);
     *x0 = __uint_as_float(w << 16);
     *x1 = __uint_as_float(w & 0xffff0000u);
   } else if (fmt == kFmtFp8) {
-    const uint32_t w = *reinterpret_cast<const uint16_t*>(page_head + slot * D + e);
+    const uint32_t w = *reinterpret_cast<const uint16_t*>(src + e);
     const uint32_t b = fp8x2_to_bf16x2<false>(w);
     *x0 = __uint_as_float(b << 16);
     *x1 = __uint_as_float(b & 0xffff0000u);
   } else {
-    // page_head points at the slot (head_dim 128): codes, then scales
-    const uint32_t code = page_head[nvfp4_code_byte(v_side, slot, e / 2)];
-    const uint32_t sb = page_head[nvfp4_scale_byte(v_side, slot, e / 16)];
+    // head_dim 128: codes, then scales
+    const uint32_t code = src[nvfp4_code_byte(v_side, slot, e / 2)];
+    const uint32_t sb = src[nvfp4_scale_byte(v_side, slot, e / 16)];
     const f16x2 sc = fp8x2_to_f16x2<false>(sb);
     const f16x2 s = {sc[0], sc[0]};
     const f16x2 v = fp4x2_to_f16x2<0>(code) * s;
@@ -49,26 +50,19 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const DequantArgs a)
   const float ks = a.k_scale ? *a.k_scale : 1.f, vs = a.v_scale ? *a.v_scale : 1.f;
   float* ko = a.k_out + ((int64_t)i * H + h) * D + e;
   float* vo = a.v_out + ((int64_t)i * H + h) * D + e;
-  const int64_t vpage = a.fmt == kFmtNvfp4 ? page : page + a.v_page_offset;
-  if (page < 0 || page >= a.num_pages || vpage >= a.num_pages) {
+  // page-16 id -> unit of the cache (the V page offset is in v_base)
+  const int64_t unit = page / a.block_page_stride * a.blk_units + page % a.block_page_stride;
+  if (page < 0 || unit >= a.num_units || unit + a.v_unit_offset >= a.num_units) {
     ko[0] = ko[1] = vo[0] = vo[1] = __builtin_nanf("");
     return;
   }
-  const uint8_t *kh, *vh;
-  if (a.fmt == kFmtNvfp4) {
-    const int slot_bytes = 9 * D;
-    kh = a.k_base + page * a.page_stride + (int64_t)(2 * h) * slot_bytes;
-    vh = kh + slot_bytes;
-  } else {
-    const int esz = a.fmt == kFmtBf16 ? 2 : 1;
-    kh = a.k_base + page * a.page_stride + (int64_t)h * kPageTokens * D * esz;
-    vh = a.v_base + vpage * a.page_stride + (int64_t)h * kPageTokens * D * esz;
-  }
+  const int64_t off = unit * a.sub_stride + (int64_t)h * a.head_stride +
+                      (a.fmt == kFmtNvfp4 ? 0 : (int64_t)slot * a.row_stride);
   float x0, x1;
-  dequant_pair(a.fmt, kh, false, slot, D, e, &x0, &x1);
+  dequant_pair(a.fmt, a.k_base + off, false, slot, e, &x0, &x1);
   ko[0] = x0 * ks;
   ko[1] = x1 * ks;
-  dequant_pair(a.fmt, vh, true, slot, D, e, &x0, &x1);
+  dequant_pair(a.fmt, a.v_base + off, true, slot, e, &x0, &x1);
   vo[0] = x0 * vs;
   vo[1] = x1 * vs;
 }

@@ -45,6 +45,95 @@ int fmt_of(int32_t kv_dtype) {
   }
 }
 
+// Layout-dependent checks of a cache descriptor (the attends and the hook).
+msa_status_t check_kv_geometry(const msa_kv_cache_t* kv) {
+  const int esz = kv->kv_dtype == MSA_BF16 ? 2 : 1;
+  int64_t page_min = 0;
+  if (kv->kv_layout == MSA_KV_PAGE16) {
+    MSA_CHECK(kv->block_page_stride == 8 || kv->block_page_stride == 16, MSA_ERR_INVALID_ARGUMENT,
+              "block_page_stride %d: 8 (separate K/V planes) or 16 (both sides in a block)", kv->block_page_stride);
+    page_min = kv->kv_dtype == MSA_NVFP4 ? (int64_t)2 * kv->num_kv_heads * 9 * kv->head_dim
+                                         : (int64_t)kv->num_kv_heads * 16 * kv->head_dim * esz;
+  } else if (kv->kv_layout == MSA_KV_ROWS128) {
+    MSA_CHECK(kv->kv_dtype != MSA_NVFP4, MSA_ERR_UNSUPPORTED, "K|V-interleaved 128-token pages hold bf16 or fp8");
+    MSA_CHECK(kv->block_page_stride == 8, MSA_ERR_INVALID_ARGUMENT,
+              "block_page_stride %d: 128-token pages need 8 (one page per block)", kv->block_page_stride);
+    MSA_CHECK(kv->v_pages == nullptr ||
+                  kv->v_pages == static_cast<const uint8_t*>(kv->k_pages) + (int64_t)kv->head_dim * esz,
+              MSA_ERR_INVALID_ARGUMENT, "v_pages must be NULL or k_pages + head_dim elements");
+    page_min = (int64_t)kv->num_kv_heads * msa::kBlockTokens * 2 * kv->head_dim * esz;
+    const int64_t sub = (int64_t)msa::kPageTokens * 2 * kv->head_dim * esz;
+    MSA_CHECK(kv->page_stride_bytes % sub == 0, MSA_ERR_INVALID_ARGUMENT,
+              "page stride %lld bytes: 128-token pages need a multiple of 16 rows (%lld bytes)",
+              (long long)kv->page_stride_bytes, (long long)sub);
+    MSA_CHECK(kv->page_stride_bytes / sub <= INT32_MAX, MSA_ERR_INVALID_ARGUMENT, "page stride %lld bytes too large",
+              (long long)kv->page_stride_bytes);
+    MSA_CHECK(kv->page_stride_bytes <= 0 || kv->num_pages <= INT64_MAX / (kv->page_stride_bytes / sub),
+              MSA_ERR_INVALID_ARGUMENT, "num_pages %lld out of range", (long long)kv->num_pages);
+  } else {
+    return fail(MSA_ERR_INVALID_ARGUMENT, "kv_layout %d: 0 (16-token pages) or 1 (K|V-interleaved 128-token pages)",
+                kv->kv_layout);
+  }
+  MSA_CHECK(kv->num_pages >= 0 && kv->num_pages <= (INT64_MAX >> 4), MSA_ERR_INVALID_ARGUMENT,
+            "num_pages %lld out of range", (long long)kv->num_pages);
+  MSA_CHECK(kv->page_stride_bytes >= page_min && kv->page_stride_bytes % 16 == 0, MSA_ERR_INVALID_ARGUMENT,
+            "page stride %lld bytes: need a multiple of 16 and >= %lld", (long long)kv->page_stride_bytes,
+            (long long)page_min);
+  return MSA_OK;
+}
+
+// The kernels' view of a checked descriptor: base pointers and strides such
+// that token t of the j-th 16-token page of block b, kv head h, starts at
+// base + (b * blk_units + j) * sub + h * head + t * row; the buffer holds
+// num_units units of sub bytes, V pages v_unit_offset units after K's.
+struct KvGeometry {
+  const uint8_t* k_base;
+  const uint8_t* v_base;
+  int32_t blk_units, head;
+  int64_t sub;
+  int32_t row;
+  int64_t num_units;
+  int32_t v_unit_offset;
+};
+
+KvGeometry kv_geometry(const msa_kv_cache_t* kv) {
+  KvGeometry g;
+  const int esz = kv->kv_dtype == MSA_BF16 ? 2 : 1;
+  const uint8_t* k = static_cast<const uint8_t*>(kv->k_pages);
+  const int64_t ps = kv->page_stride_bytes;
+  if (kv->kv_layout == MSA_KV_ROWS128) {
+    const int32_t row = 2 * kv->head_dim * esz;
+    g.k_base = k;
+    g.v_base = k ? k + (int64_t)kv->head_dim * esz : nullptr;
+    g.sub = (int64_t)msa::kPageTokens * row;
+    g.blk_units = (int32_t)(ps / g.sub);
+    g.head = msa::kBlockTokens * row;
+    g.row = row;
+    g.num_units = kv->num_pages * g.blk_units;
+    g.v_unit_offset = 0;
+  } else if (kv->kv_dtype == MSA_NVFP4) {
+    g.k_base = k;
+    g.v_base = k ? k + 9 * kv->head_dim : nullptr;
+    g.sub = ps;
+    g.blk_units = kv->block_page_stride;
+    g.head = 2 * 9 * kv->head_dim;
+    g.row = 0;
+    g.num_units = kv->num_pages;
+    g.v_unit_offset = 0;
+  } else {
+    const int32_t row = kv->head_dim * esz;
+    g.v_unit_offset = kv->block_page_stride - msa::kPagesPerBlock;
+    g.k_base = k;
+    g.v_base = kv->v_pages ? static_cast<const uint8_t*>(kv->v_pages) + g.v_unit_offset * ps : nullptr;
+    g.sub = ps;
+    g.blk_units = kv->block_page_stride;
+    g.head = msa::kPageTokens * row;
+    g.row = row;
+    g.num_units = kv->num_pages;
+  }
+  return g;
+}
+
 // Validation shared by the attends.
 msa_status_t check_attend(const void* q, int32_t q_dtype, int32_t rows, int32_t num_q_heads, const msa_kv_cache_t* kv,
                           const int32_t* topk, int64_t topk_row_stride, int32_t topk_k, const int32_t* block_table,
@@ -63,27 +152,23 @@ msa_status_t check_attend(const void* q, int32_t q_dtype, int32_t rows, int32_t 
             "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, kv->num_kv_heads);
   MSA_CHECK(num_q_heads / kv->num_kv_heads <= 16, MSA_ERR_UNSUPPORTED,
             "%d query heads per kv head: at most 16 are served", num_q_heads / kv->num_kv_heads);
-  MSA_CHECK(kv->block_page_stride == 8 || kv->block_page_stride == 16, MSA_ERR_INVALID_ARGUMENT,
-            "block_page_stride %d: 8 (separate K/V planes) or 16 (both sides in a block)", kv->block_page_stride);
+  {
+    const msa_status_t st = check_kv_geometry(kv);
+    if (st != MSA_OK) return st;
+  }
   MSA_CHECK(topk_k >= 1 && topk_k <= msa::kMaxTopK, MSA_ERR_UNSUPPORTED, "topk_k %d: 1..%d", topk_k, msa::kMaxTopK);
   MSA_CHECK(topk_row_stride >= topk_k, MSA_ERR_INVALID_ARGUMENT, "topk row stride %lld < topk_k %d",
             (long long)topk_row_stride, topk_k);
   MSA_CHECK(bt_cols >= 0 && bt_row_stride >= bt_cols, MSA_ERR_INVALID_ARGUMENT,
             "block_table: %d columns, row stride %lld", bt_cols, (long long)bt_row_stride);
-  MSA_CHECK(kv->num_pages >= 0, MSA_ERR_INVALID_ARGUMENT, "num_pages %lld < 0", (long long)kv->num_pages);
-  const int esz = kv->kv_dtype == MSA_BF16 ? 2 : 1;
-  const int64_t page_min = kv->kv_dtype == MSA_NVFP4 ? (int64_t)2 * kv->num_kv_heads * 9 * kv->head_dim
-                                                      : (int64_t)kv->num_kv_heads * 16 * kv->head_dim * esz;
-  MSA_CHECK(kv->page_stride_bytes >= page_min && kv->page_stride_bytes % 16 == 0, MSA_ERR_INVALID_ARGUMENT,
-            "page stride %lld bytes: need a multiple of 16 and >= %lld", (long long)kv->page_stride_bytes,
-            (long long)page_min);
   MSA_CHECK(softmax_scale == softmax_scale, MSA_ERR_INVALID_ARGUMENT, "softmax_scale is NaN");
   if (rows > 0) {
     MSA_CHECK(q && out && topk && block_table && kv->k_pages, MSA_ERR_INVALID_ARGUMENT,
               "q, out, topk, block_table and k_pages must be non-NULL");
-    MSA_CHECK(kv->kv_dtype == MSA_NVFP4 || kv->v_pages, MSA_ERR_INVALID_ARGUMENT, "v_pages is NULL");
+    const bool v_plane = kv->kv_dtype != MSA_NVFP4 && kv->kv_layout == MSA_KV_PAGE16;
+    MSA_CHECK(!v_plane || kv->v_pages, MSA_ERR_INVALID_ARGUMENT, "v_pages is NULL");
     MSA_CHECK(((uintptr_t)q % 16) == 0 && ((uintptr_t)out % 16) == 0 && ((uintptr_t)kv->k_pages % 16) == 0 &&
-                  (kv->kv_dtype == MSA_NVFP4 || ((uintptr_t)kv->v_pages % 16) == 0),
+                  (!v_plane || ((uintptr_t)kv->v_pages % 16) == 0),
               MSA_ERR_INVALID_ARGUMENT, "q, out and page buffers must be 16-byte aligned");
   }
   return MSA_OK;
@@ -115,12 +200,15 @@ msa::AttendArgs attend_args(const void* q, int32_t num_q_heads, const msa_kv_cac
   a.block_table = block_table;
   a.bt_stride = bt_row_stride;
   a.bt_cols = bt_cols;
-  a.k_base = static_cast<const uint8_t*>(kv->k_pages);
-  a.v_base = static_cast<const uint8_t*>(kv->kv_dtype == MSA_NVFP4 ? kv->k_pages : kv->v_pages);
-  a.page_stride = kv->page_stride_bytes;
-  a.num_pages = kv->num_pages;
-  a.block_page_stride = kv->block_page_stride;
-  a.v_page_offset = kv->kv_dtype == MSA_NVFP4 ? 0 : kv->block_page_stride - msa::kPagesPerBlock;
+  const KvGeometry g = kv_geometry(kv);
+  a.k_base = g.k_base;
+  a.v_base = g.v_base;
+  a.blk_units = g.blk_units;
+  a.sub_stride = g.sub;
+  a.head_stride = g.head;
+  a.row_stride = g.row;
+  a.num_units = g.num_units;
+  a.v_unit_offset = g.v_unit_offset;
   a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale;
   a.softmax_scale = softmax_scale;
@@ -389,20 +477,30 @@ MSA_API msa_status_t msa_debug_dequant_tokens(const msa_kv_cache_t* kv, const in
   MSA_CHECK(fmt_of(kv->kv_dtype) >= 0, MSA_ERR_UNSUPPORTED, "kv dtype %d", kv->kv_dtype);
   MSA_CHECK(kv->head_dim >= 16 && kv->head_dim % 16 == 0 && kv->num_kv_heads >= 1, MSA_ERR_INVALID_ARGUMENT,
             "head_dim %d / num_kv_heads %d", kv->head_dim, kv->num_kv_heads);
-  MSA_CHECK(kv->block_page_stride == 8 || kv->block_page_stride == 16, MSA_ERR_INVALID_ARGUMENT,
-            "block_page_stride %d", kv->block_page_stride);
+  MSA_CHECK(kv->kv_dtype != MSA_NVFP4 || kv->head_dim == 128, MSA_ERR_UNSUPPORTED,
+            "nvfp4 pages need head_dim 128 (got %d)", kv->head_dim);
+  {
+    const msa_status_t st = check_kv_geometry(kv);
+    if (st != MSA_OK) return st;
+  }
   if (n == 0) return ok();
-  MSA_CHECK(pages && slots && k_out && v_out && kv->k_pages && (kv->kv_dtype == MSA_NVFP4 || kv->v_pages),
+  const bool v_plane = kv->kv_dtype != MSA_NVFP4 && kv->kv_layout == MSA_KV_PAGE16;
+  MSA_CHECK(pages && slots && k_out && v_out && kv->k_pages && (!v_plane || kv->v_pages),
             MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   msa::DequantArgs a;
+  const KvGeometry g = kv_geometry(kv);
   a.fmt = fmt_of(kv->kv_dtype);
   a.num_kv_heads = kv->num_kv_heads;
   a.head_dim = kv->head_dim;
-  a.v_page_offset = kv->kv_dtype == MSA_NVFP4 ? 0 : kv->block_page_stride - msa::kPagesPerBlock;
-  a.k_base = static_cast<const uint8_t*>(kv->k_pages);
-  a.v_base = static_cast<const uint8_t*>(kv->kv_dtype == MSA_NVFP4 ? kv->k_pages : kv->v_pages);
-  a.page_stride = kv->page_stride_bytes;
-  a.num_pages = kv->num_pages;
+  a.block_page_stride = kv->block_page_stride;
+  a.k_base = g.k_base;
+  a.v_base = g.v_base;
+  a.blk_units = g.blk_units;
+  a.sub_stride = g.sub;
+  a.head_stride = g.head;
+  a.row_stride = g.row;
+  a.num_units = g.num_units;
+  a.v_unit_offset = g.v_unit_offset;
   a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale;
   a.pages = pages;

@@ -22,12 +22,23 @@ struct AttendArgs {
   const int32_t* cu_seqlens_q;
   int32_t dql;
   int32_t num_reqs;
+  // Cache geometry, in units of sub_stride bytes (one 16-token page of one
+  // layer).  Token t (0..15) of the j-th 16-token page (j < 8) of sparse
+  // block `phys`, kv head h, starts at
+  //   k_base + (phys * blk_units + j) * sub_stride + h * head_stride + t * row_stride
+  // (NVFP4: the K slot of head h, token rows inside the slot as the format
+  // gives them); V at the same offsets from v_base, which has the V page
+  // offset, the V slot or the in-row offset of V folded in.  A block's
+  // pages are inside the cache when phys * blk_units + v_unit_offset + 7 <
+  // num_units.
   const uint8_t* k_base;
   const uint8_t* v_base;
-  int64_t page_stride;
-  int64_t num_pages;
-  int32_t block_page_stride;
-  int32_t v_page_offset;
+  int32_t blk_units;
+  int32_t head_stride;
+  int64_t sub_stride;
+  int32_t row_stride;
+  int64_t num_units;
+  int32_t v_unit_offset;
   const float* k_scale;
   const float* v_scale;
   float softmax_scale;
@@ -81,11 +92,15 @@ struct DequantArgs {
   int fmt;
   int num_kv_heads;
   int head_dim;
-  int v_page_offset;
-  const uint8_t* k_base;
+  int block_page_stride;    // page-16 id p names page p % block_page_stride of block p / block_page_stride
+  const uint8_t* k_base;   // geometry as in AttendArgs
   const uint8_t* v_base;
-  int64_t page_stride;
-  int64_t num_pages;
+  int32_t blk_units;
+  int32_t head_stride;
+  int64_t sub_stride;
+  int32_t row_stride;
+  int64_t num_units;
+  int32_t v_unit_offset;
   const float* k_scale;
   const float* v_scale;
   const int32_t* pages;

@@ -86,26 +86,25 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void pf_issue_part(lds_u8* kb, lds_u8* vb, const AttendArgs& a, int kvh, int phys,
                                               int blk, int seq_len, int part) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t pg = (int64_t)phys * a.block_page_stride;
-  const int64_t head_off = (int64_t)kvh * kPageTokens * 256;
+  const int64_t boff = (int64_t)phys * a.blk_units * a.sub_stride + (int64_t)kvh * a.head_stride;
+  const int rs = a.row_stride;
   const int nkeys = seq_len - blk * kBlockTokens;     // keys of this block that exist (>= 1)
   const int unit = wave * 4 + part;                   // 1 KB unit of the 32 KB block this wave fills
   const int kkey = 16 * wave + 4 * part + (lane >> 4), kpc = lane & 15;
   const int vkey = 32 * part + (lane >> 1), vlc = 2 * wave + (lane & 1);
-  if (nkeys >= kBlockTokens && a.page_stride < (int64_t(1) << 30)) {
-    const uint8_t* kbase = a.k_base + (pg + wave) * a.page_stride + head_off;
-    const uint8_t* vbase = a.v_base + (pg + a.v_page_offset + 2 * part) * a.page_stride + head_off;
-    const uint32_t koff = (uint32_t)((kkey & 15) * 256 + ((kpc ^ k_swz(kkey)) << 4));
-    const uint32_t voff = (uint32_t)((lane >> 5) * a.page_stride + (vkey & 15) * 256 + (vlc << 4));
+  if (nkeys >= kBlockTokens && a.sub_stride < (int64_t(1) << 30)) {
+    const uint8_t* kbase = a.k_base + boff + wave * a.sub_stride;
+    const uint8_t* vbase = a.v_base + boff + 2 * part * a.sub_stride;
+    const uint32_t koff = (uint32_t)((kkey & 15) * rs + ((kpc ^ k_swz(kkey)) << 4));
+    const uint32_t voff = (uint32_t)((lane >> 5) * a.sub_stride + (vkey & 15) * rs + (vlc << 4));
     __builtin_amdgcn_global_load_lds(kbase + koff, kb + unit * 1024, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vbase + voff, vb + unit * 1024, 16, 0, 0);
   } else {
     const int ks = kkey < nkeys ? kkey : 0, vs = vkey < nkeys ? vkey : 0;
-    __builtin_amdgcn_global_load_lds(a.k_base + (pg + (ks >> 4)) * a.page_stride + head_off + (ks & 15) * 256 +
+    __builtin_amdgcn_global_load_lds(a.k_base + boff + (ks >> 4) * a.sub_stride + (ks & 15) * rs +
                                          ((kpc ^ k_swz(kkey)) << 4),
                                      kb + unit * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(a.v_base + (pg + a.v_page_offset + (vs >> 4)) * a.page_stride + head_off +
-                                         (vs & 15) * 256 + (vlc << 4),
+    __builtin_amdgcn_global_load_lds(a.v_base + boff + (vs >> 4) * a.sub_stride + (vs & 15) * rs + (vlc << 4),
                                      vb + unit * 1024, 16, 0, 0);
   }
 }
@@ -296,31 +295,30 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* k
 template <int FMT>
 __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a, int kvh, int phys) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t pg = (int64_t)phys * a.block_page_stride;
+  const int64_t boff = (int64_t)phys * a.blk_units * a.sub_stride + (int64_t)kvh * a.head_stride;
   if constexpr (FMT == kFmtFp8) {
-    const int64_t head_off = (int64_t)kvh * kPageTokens * 128;
+    const int rs = a.row_stride;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int q = k * kPfThreads + wave * 64 + lane;
       const uint8_t* src;
       if (k < 2) {
         const int key = q >> 3, n = q & 7;
-        src = a.k_base + (pg + (key >> 4)) * a.page_stride + head_off + (key & 15) * 128 + 16 * n;
+        src = a.k_base + boff + (key >> 4) * a.sub_stride + (key & 15) * rs + 16 * n;
       } else {
         const int q2 = q - 1024, n = q2 >> 7, key = q2 & 127;
-        src = a.v_base + (pg + a.v_page_offset + (key >> 4)) * a.page_stride + head_off + (key & 15) * 128 + 16 * n;
+        src = a.v_base + boff + (key >> 4) * a.sub_stride + (key & 15) * rs + 16 * n;
       }
       __builtin_amdgcn_global_load_lds(src, raw + (k * kPfThreads + wave * 64) * 16, 16, 0, 0);
     }
   } else {
     constexpr int SLOT = 9 * 128, PAGE_PIECES = 2 * SLOT / 16;   // 144 pieces of 16 B per page
-    const int64_t head_off = (int64_t)(2 * kvh) * SLOT;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       if (k == 2 && wave >= 2) break;   // 1152 pieces: the third pass is two waves
       const int q = k * kPfThreads + wave * 64 + lane;
       const int page = q / PAGE_PIECES, off = (q - page * PAGE_PIECES) * 16;
-      __builtin_amdgcn_global_load_lds(a.k_base + (pg + page) * a.page_stride + head_off + off,
+      __builtin_amdgcn_global_load_lds(a.k_base + boff + page * a.sub_stride + off,
                                        raw + (k * kPfThreads + wave * 64) * 16, 16, 0, 0);
     }
   }
@@ -481,8 +479,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
       bool act = j < nblk && s_mask[j] != 0u;
       if (act) {
         const int phys = bt_row[j];
-        const int64_t last = (int64_t)phys * a.block_page_stride + a.v_page_offset + kPagesPerBlock - 1;
-        act = phys >= 0 && last < a.num_pages;
+        const int64_t last = (int64_t)phys * a.blk_units + a.v_unit_offset + kPagesPerBlock - 1;
+        act = phys >= 0 && last < a.num_units;
       }
       const uint64_t am = __ballot(act);
       const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(am >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)am, 0u));

@@ -61,12 +61,19 @@ typedef enum msa_dtype {
   MSA_FP32 = 4
 } msa_dtype_t;
 
+/* How a cache's pages are laid out (msa_kv_cache_t.kv_layout). */
+typedef enum msa_kv_layout {
+  MSA_KV_PAGE16 = 0,    /* 16-token pages: K and V planes, or NVFP4 head slots */
+  MSA_KV_ROWS128 = 1    /* 128-token pages with K|V-interleaved token rows */
+} msa_kv_layout_t;
+
 /*
  * One layer's paged K/V cache.  [FI] MiniMaxM3SparseFlashInferImpl.forward
  * (K and V views of the cache, fp8 view with per-tensor scales);
  * [NV4] customize_spec (NVFP4: two head slots per kv head, packed data plus
  * block scales, bytes laid out for the kernel).
  *
+ * kv_layout MSA_KV_PAGE16 (0, the default):
  * kv_dtype MSA_BF16 / MSA_FP8_E4M3FN: K and V are planes of pages
  *   [page][num_kv_heads][16 tokens][head_dim] elements, page p at byte
  *   p * page_stride_bytes of its buffer.  With block_page_stride 8, block b
@@ -86,13 +93,25 @@ typedef enum msa_dtype {
  *       (the decode reads one token group's 8 elements and their 4 scales
  *       with one load each).
  *
+ * kv_layout MSA_KV_ROWS128 (bf16 / fp8 only; [FI] MiniMaxM3SparseFlashInfer-
+ *   Backend.supported_kv_cache_layouts: the head-major LBHNC cache the SM90
+ *   kernels read): one buffer k_pages of pages
+ *   [page][num_kv_heads][128 tokens][2 * head_dim] elements, each token row
+ *   holding its K (elements 0 .. head_dim - 1) then its V; page p at byte
+ *   p * page_stride_bytes, a multiple of 16 rows (16 * 2 * head_dim
+ *   elements; a stride above the page size packs other data, e.g. other
+ *   layers, between pages).  Page b is sparse block b, so
+ *   block_page_stride must be 8: page-16 id 8b + j (the table builder's ids)
+ *   names rows 16j .. 16j + 15 of page b.  v_pages is NULL or
+ *   k_pages + head_dim elements (the V view of the same buffer).
+ *
  * k_scale / v_scale: device fp32 scalars (NULL = 1.0).  fp8: the
  *   per-tensor dequant multipliers; NVFP4: the per-tensor global scales.
  *   They fold exactly into the softmax scale and the output scale
  *   ([FI] forward: logits are linear in K, the output in V).
- * num_pages: pages each buffer holds.  Blocks whose pages fall outside
- *   [0, num_pages) are skipped (they add nothing), so a bad table cannot
- *   make the attend read out of bounds.
+ * num_pages: pages each buffer holds (MSA_KV_ROWS128: 128-token pages).
+ *   Blocks whose pages fall outside [0, num_pages) are skipped (they add
+ *   nothing), so a bad table cannot make the attend read out of bounds.
  */
 typedef struct msa_kv_cache {
   int32_t kv_dtype;
@@ -105,6 +124,7 @@ typedef struct msa_kv_cache {
   int64_t num_pages;
   const float* k_scale;
   const float* v_scale;
+  int32_t kv_layout;   /* msa_kv_layout_t */
 } msa_kv_cache_t;
 
 /* Thread-local description of the last error returned on this thread. */

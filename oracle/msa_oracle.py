@@ -275,12 +275,21 @@ class PagedKVCache:
     when K and V are separate planes and 16 when a block holds both sides;
     reading: then V of page p is page p + 8 of the V buffer ("reached from
     the same page id at a fixed offset").
+
+    ``layout="rows128"`` (bf16 / fp8): k_pages is the one dense
+    [pages, Hkv, 128, 2 * D] array of [FI] MiniMaxM3SparseFlashInferBackend.
+    supported_kv_cache_layouts, each token row holding K then V; v_pages is
+    unused.  Reading: page b is sparse block b and page-16 id
+    b * block_page_stride + j names its rows 16 j .. 16 j + 15.
     """
 
     def __init__(self, kv_dtype, k_pages, v_pages, num_kv_heads, head_dim,
-                 block_page_stride=PAGES_PER_SPARSE_BLOCK, k_scale=1.0, v_scale=1.0):
+                 block_page_stride=PAGES_PER_SPARSE_BLOCK, k_scale=1.0, v_scale=1.0, layout="page16"):
         if kv_dtype not in ("bf16", "fp8", "nvfp4"):
             raise ValueError(kv_dtype)
+        if layout not in ("page16", "rows128") or (layout == "rows128" and kv_dtype == "nvfp4"):
+            raise ValueError(layout)
+        self.layout = layout
         self.kv_dtype = kv_dtype
         self.k_pages = k_pages
         self.v_pages = v_pages
@@ -300,7 +309,13 @@ class PagedKVCache:
             g = self.k_scale if side == "k" else self.v_scale
             tok = np.broadcast_to(slots[:, None], raw.shape[:2])
             return nvfp4_token_values(raw, tok, self.head_dim, g, side)
-        if side == "k":
+        if self.layout == "rows128":
+            D = self.head_dim
+            blk, j = pages // self.block_page_stride, pages % self.block_page_stride
+            row = self.k_pages[blk, :, PAGE_SIZE * j + slots, :]              # [n, Hkv, 2D]
+            raw = row[..., :D] if side == "k" else row[..., D:]
+            scale = self.k_scale if side == "k" else self.v_scale
+        elif side == "k":
             raw, scale = self.k_pages[pages, :, slots, :], self.k_scale
         else:
             off = self.block_page_stride - PAGES_PER_SPARSE_BLOCK

@@ -34,7 +34,7 @@ import torch
 __all__ = [
     "Workload", "CONFIGS", "make_workload", "make_query", "make_kv_cache",
     "encode_fp8_e4m3fn", "encode_nvfp4_rows", "arrange_nvfp4_slot", "NAN_BYTE",
-    "written_blocks",
+    "written_blocks", "rows128_cache",
 ]
 
 BLOCK = 128          # tokens per sparse block
@@ -331,4 +331,34 @@ def make_kv_cache(wl, device="cpu"):
         k_pages = k_pages.view(num_pages, 2 * Hkv, slot_bytes)
         v_pages = None
     return dict(k_pages=k_pages, v_pages=v_pages, k_scale=k_scale, v_scale=v_scale,
-                page_stride_bytes=page_bytes, num_pages=num_pages)
+                page_stride_bytes=page_bytes, num_pages=num_pages, layout="page16")
+
+
+def rows128_cache(cache, wl, layers=1, layer=0):
+    """The same bf16 / fp8 cache re-laid as 128-token pages with K|V rows.
+
+    Page b (= sparse block b) is [Hkv, 128 tokens, K row bytes then V row
+    bytes]; with ``layers`` > 1 the pages sit in a block-outer buffer, page b
+    of this layer at (b * layers + layer) * page bytes, the other layers'
+    bytes NaN-filled.  Needs a cache of block_page_stride 8.  Returns a dict
+    like make_kv_cache's: ``k_pages`` [blocks, Hkv, 128, 2 * row] uint8,
+    ``v_pages`` None, ``layout`` "rows128".
+    """
+    if wl.kv_dtype not in ("bf16", "fp8") or wl.block_page_stride != PAGES_PER_BLOCK:
+        raise ValueError("rows128 holds bf16 / fp8 caches of block_page_stride 8")
+    k, v = cache["k_pages"], cache["v_pages"]
+    n16, Hkv, _, row = k.shape
+    nb = n16 // PAGES_PER_BLOCK
+
+    def per_block(t):   # [n16, Hkv, 16, row] -> [nb, Hkv, 128, row]
+        return t.reshape(nb, PAGES_PER_BLOCK, Hkv, PAGE, row).permute(0, 2, 1, 3, 4).reshape(nb, Hkv, BLOCK, row)
+
+    rows = torch.cat([per_block(k), per_block(v)], dim=-1)           # [nb, Hkv, 128, 2 row]
+    page_bytes = Hkv * BLOCK * 2 * row
+    big = torch.full((nb, layers, page_bytes), NAN_BYTE, dtype=torch.uint8, device=k.device)
+    big[:, layer] = rows.reshape(nb, page_bytes)
+    pages = big[:, layer].view(nb, Hkv, BLOCK, 2 * row)
+    out = dict(cache)
+    out.update(k_pages=pages, v_pages=None, page_stride_bytes=layers * page_bytes, num_pages=nb,
+               layout="rows128")
+    return out

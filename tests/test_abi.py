@@ -75,7 +75,8 @@ def test_index_cache_needs_contiguous_head_dim():
 
 def _kv(**kw):
     d = dict(kv_dtype=msa.MSA_BF16, num_kv_heads=8, head_dim=128, block_page_stride=8, k_pages=0x1000,
-             v_pages=0x2000, page_stride_bytes=8 * 16 * 128 * 2, num_pages=64, k_scale=None, v_scale=None)
+             v_pages=0x2000, page_stride_bytes=8 * 16 * 128 * 2, num_pages=64, k_scale=None, v_scale=None,
+             kv_layout=0)
     d.update(kw)
     return msa._KV(*d.values())
 
@@ -106,6 +107,26 @@ def test_decode_argument_errors(kvkw, kw, status):
 
 def test_decode_empty_batch_is_noop():
     assert _decode(_kv(), num_reqs=0) == 0
+
+
+ROWS128 = dict(kv_layout=1, v_pages=None, page_stride_bytes=8 * 128 * 2 * 128 * 2)
+
+
+@pytest.mark.parametrize("kvkw,status", [
+    (dict(ROWS128), 0),                                          # valid (empty batch: nothing runs)
+    (dict(ROWS128, v_pages=0x1000 + 256), 0),                    # V view of the same buffer
+    (dict(ROWS128, v_pages=0x2000), 1),                          # V elsewhere
+    (dict(ROWS128, block_page_stride=16), 1),                    # one page per block
+    (dict(ROWS128, page_stride_bytes=8 * 16 * 128 * 2), 1),     # smaller than a 128-token page
+    (dict(ROWS128, page_stride_bytes=8 * 128 * 2 * 128 * 2 + 4096), 1),   # not a multiple of 16 rows
+    (dict(ROWS128, page_stride_bytes=3 * 8 * 128 * 2 * 128 * 2), 0),      # three layers, block-outer
+    (dict(ROWS128, kv_dtype=msa.MSA_NVFP4, page_stride_bytes=1 << 20), 2),
+    (dict(kv_layout=2), 1),
+])
+def test_rows128_layout_checks(kvkw, status):
+    assert _decode(_kv(**kvkw), num_reqs=0) == status
+    if status:
+        assert _decode(_kv(**kvkw)) == status
 
 
 def test_prefill_rejects_unsupported_shapes():

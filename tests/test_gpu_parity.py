@@ -2,8 +2,10 @@
 
 Bit-exact: sparse block table, context lengths, prefill positions, dequant
 hook, index-cache insert.  Attention: max |GPU - oracle| <= 1e-2 (the bound
-the method's acceptance states for bf16 outputs on N(0, 1) inputs), with
-every unread byte of the cache NaN-poisoned.
+the method's acceptance states for bf16 outputs on N(0, 1) inputs) wherever
+|oracle| < 4; above, where bf16 values are 1/32 apart, the output must be
+one of the two bf16 neighbours of the oracle value.  Every unread byte of
+the cache is NaN-poisoned.
 """
 
 import numpy as np
@@ -12,8 +14,8 @@ import torch
 
 import oracle
 import block_sparse_paged_query_amd as msa
-from synth import make_workload, make_kv_cache, make_query, written_blocks
-from tests.helpers import compact_oracle_inputs, oracle_cache, oracle_positions, q_f64
+from synth import make_workload, make_kv_cache, make_query, rows128_cache, written_blocks
+from tests.helpers import attention_within_tolerance, compact_oracle_inputs, oracle_cache, oracle_positions, q_f64
 
 pytestmark = pytest.mark.gpu
 ATOL = 1e-2
@@ -30,7 +32,7 @@ def _kv(wl, cache):
         ks = torch.tensor([cache["k_scale"]], dtype=torch.float32, device=DEV)
         vs = torch.tensor([cache["v_scale"]], dtype=torch.float32, device=DEV)
     return msa.KVCache(wl.kv_dtype, cache["k_pages"], cache["v_pages"], wl.num_kv_heads, wl.head_dim,
-                       wl.block_page_stride, ks, vs)
+                       wl.block_page_stride, ks, vs, layout=cache.get("layout", "page16"))
 
 
 def _run(wl, cache, q):
@@ -100,10 +102,13 @@ def _hook_vs_oracle(wl, cache, pages, slots):
         assert (got[~nan].view(np.uint32) == want[~nan].view(np.uint32)).all()
 
 
-@pytest.mark.parametrize("name", ["C3s", "C5s", "C2s"])
-def test_dequant_hook_bit_exact_on_written_tokens(name):
+@pytest.mark.parametrize("name,layout", [("C3s", "page16"), ("C5s", "page16"), ("C2s", "page16"),
+                                         ("C2s", "rows128"), ("C3s", "rows128")])
+def test_dequant_hook_bit_exact_on_written_tokens(name, layout):
     wl = make_workload(name)
     cache = make_kv_cache(wl, DEV)
+    if layout == "rows128":
+        cache = rows128_cache(cache, wl, layers=2, layer=1)
     pages, slots = [], []
     for (r, b, n) in written_blocks(wl):
         phys = int(wl.block_table[r, b])
@@ -138,8 +143,8 @@ def test_dequant_hook_exhaustive_codes():
 
 # ---------------------------------------------------------------- attention
 
-def _parity(wl, rows=None):
-    cache = make_kv_cache(wl, DEV)
+def _parity(wl, rows=None, cache=None):
+    cache = make_kv_cache(wl, DEV) if cache is None else cache
     q = make_query(wl, DEV)
     out = _run(wl, cache, q)
     req, pos = oracle_positions(wl)
@@ -150,8 +155,8 @@ def _parity(wl, rows=None):
     want = oracle.sparse_attention(qf, oc, wl.topk, bt, req, pos, wl.softmax_scale, rows=rows)
     got = out.float().cpu().numpy()[rows]
     assert np.isfinite(got).all()
-    err = np.abs(got - want).max()
-    assert err <= ATOL, f"max abs error {err}"
+    ok, err, n_big = attention_within_tolerance(got, want, ATOL)
+    assert ok, f"max abs error {err} (|want| < 4), {n_big} elements checked for faithful rounding"
     return out, err
 
 
@@ -248,6 +253,29 @@ def test_block_outer_page_stride(name, kw):
     assert torch.equal(dense, got)
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("C2s", {}), ("C3s", {}), ("C3s", dict(D=64, Hq=16, Hkv=8, k=8, seed=31)),
+    ("C4s", {}), ("C4s", dict(kv_dtype="fp8")), ("C4s", dict(Hq=16, Hkv=4, seed=42)),
+    ("C4s", dict(kv_dtype="fp8", qlens=[1, 40, 700], context=[3000, 0, 129], seed=45)),
+])
+def test_rows128_layout(name, kw):
+    # [FI] MiniMaxM3SparseFlashInferBackend.supported_kv_cache_layouts: one
+    # dense (pages, kv heads, 128, 2 * head_dim) cache, K and V interleaved
+    # per token row.  The same tokens re-laid that way (alone, and packed
+    # block-outer with two other layers) give the oracle's result and exactly
+    # the 16-token-page layout's output.
+    wl = make_workload(name, **kw)
+    cache = make_kv_cache(wl, DEV)
+    q = make_query(wl, DEV)
+    dense = _run(wl, cache, q)
+    rows = rows128_cache(cache, wl)
+    assert _kv(wl, rows)._struct().kv_layout == 1
+    got, _ = _parity(wl, cache=rows)
+    assert torch.equal(dense, got)
+    packed = rows128_cache(cache, wl, layers=3, layer=2)
+    assert torch.equal(dense, _run(wl, packed, q))
+
+
 @pytest.mark.parametrize("dql", [1, 2])
 def test_mixed_batch_matches_separate_calls(dql):
     # [FI] forward: decode tokens first, then prefill tokens, one cache, one
@@ -282,7 +310,7 @@ def test_mixed_batch_matches_separate_calls(dql):
         rows = np.arange(wl.total_q)
         oc, bt, _, _ = compact_oracle_inputs(wl, cache, rows)
         want = oracle.sparse_attention(q_f64(qq), oc, wl.topk, bt, req, pos, wl.softmax_scale, rows=rows)
-        assert np.abs(got.float().cpu().numpy() - want).max() <= ATOL
+        assert attention_within_tolerance(got.float().cpu().numpy(), want, ATOL)[0]
 
 
 def test_mixed_batch_in_a_graph():
