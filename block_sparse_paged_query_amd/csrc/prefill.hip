@@ -85,7 +85,13 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // probability zero), so no NaN of an unwritten slot reaches the products.
 __device__ __forceinline__ void pf_issue_part(lds_u8* kb, lds_u8* vb, const AttendArgs& a, int kvh, int phys,
                                               int blk, int seq_len, int part) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // (block ids come from LDS: make their uniformity explicit so that the
+  // bases below are scalar and only 32-bit lane offsets stay in registers)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));   // recompute the lane offsets here rather than keep them live across blocks
+  phys = __builtin_amdgcn_readfirstlane(phys);
+  blk = __builtin_amdgcn_readfirstlane(blk);
   const int64_t boff = (int64_t)phys * a.blk_units * a.sub_stride + (int64_t)kvh * a.head_stride;
   const int rs = a.row_stride;
   const int nkeys = seq_len - blk * kBlockTokens;     // keys of this block that exist (>= 1)
@@ -133,10 +139,14 @@ constexpr float kLazy = 8.f;
 // softmaxes (one uniform branch covers the rare rescale of any tile), then all
 // PV products.  A tile's softmax runs while the next tile's products are in
 // the matrix pipe, and its PV products while the next softmax runs.
-template <int MASK, class OT>
-__device__ __forceinline__ void pf_chunk(PfWave<OT>& w, const OT (&kop)[2][PfWave<OT>::KK], const OT (&vop)[PfWave<OT>::NN],
+// `next_k` / `next_v` refill the K / V operand registers with the next
+// chunk's once this chunk's products have consumed them, so those LDS reads
+// overlap this chunk's softmax and PV work instead of stalling the next
+// chunk's first product.
+template <int MASK, class OT, class NextK, class NextV>
+__device__ __forceinline__ void pf_chunk(PfWave<OT>& w, OT (&kop)[2][PfWave<OT>::KK], OT (&vop)[PfWave<OT>::NN],
                                          const float (&bias)[kPfTiles], const OT& ones, float sl2, bool causal,
-                                         int kbase) {
+                                         int kbase, NextK&& next_k, NextV&& next_v) {
   constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
   constexpr bool kF16 = __is_same(OT, f16x8);
   float sv[kPfTiles][8];
@@ -155,6 +165,8 @@ __device__ __forceinline__ void pf_chunk(PfWave<OT>& w, const OT (&kop)[2][PfWav
       sv[i][4 + ii] = s1[ii];
     }
   }
+  __builtin_amdgcn_sched_barrier(0);   // the refill must not rise above the products reading kop
+  next_k(kop);
   float mxs[kPfTiles];
   bool need = false;
 #pragma unroll
@@ -205,6 +217,8 @@ __device__ __forceinline__ void pf_chunk(PfWave<OT>& w, const OT (&kop)[2][PfWav
     for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = mfma16(vop[nn], pop, w.acc[i][nn]);
     w.lacc[i] = mfma16(ones, pop, w.lacc[i]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  next_v(vop);
 }
 
 struct PfNext {       // the block whose copies are issued during this one
@@ -213,6 +227,45 @@ struct PfNext {       // the block whose copies are issued during this one
   int phys, blk;
   bool valid;
 };
+
+// The block's four 32-key chunks against the tiles in MASK.  Each chunk's K
+// and V operands (shared by the wave's active tiles) are read from LDS while
+// the previous chunk computes.
+template <int MASK, class OT>
+__device__ __forceinline__ void pf_chunks(PfWave<OT>& w, const uint8_t* kb, const uint8_t* vb,
+                                          const int (&koff)[PfWave<OT>::KK], int voff,
+                                          const float (&bias)[kPfTiles], const OT& ones, float sl2, bool causal,
+                                          int kbase0) {
+  constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
+  auto load_k = [&](OT (&kop)[2][KK], int c) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kop[tt][kk] = *reinterpret_cast<const OT*>(kb + (c * 32 + 16 * tt) * 256 + koff[kk]);
+  };
+  auto load_v = [&](OT (&vop)[NN], int c) {
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) {
+      const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (v4i16 __attribute__((address_space(3)))*)((const lds_u8*)vb + nn * 4096 + c * 1024 + voff));
+      const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (v4i16 __attribute__((address_space(3)))*)((const lds_u8*)vb + nn * 4096 + c * 1024 + 512 + voff));
+      const u32x2 l0 = __builtin_bit_cast(u32x2, h0), l1 = __builtin_bit_cast(u32x2, h1);
+      vop[nn] = __builtin_bit_cast(OT, u32x4{l0[0], l0[1], l1[0], l1[1]});
+    }
+  };
+  OT kop[2][KK];
+  OT vop[NN];
+  load_k(kop, 0);
+  load_v(vop, 0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    pf_chunk<MASK, OT>(w, kop, vop, bias, ones, sl2, causal, kbase0 + c * 32,
+                       [&](OT (&k)[2][KK]) { if (c < 3) load_k(k, c + 1); },
+                       [&](OT (&v)[NN]) { if (c < 3) load_v(v, c + 1); });
+  }
+}
 
 // One selected block against this wave's tiles.  `causal` is set when the
 // block can be the own block of a row of this workgroup (keys past a row's
@@ -252,34 +305,9 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* k
 #pragma unroll
     for (int part = 0; part < 4; ++part) pf_issue_part(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len, part);
   }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    OT kop[2][KK];
-    OT vop[NN];
-    if (tiles) {
-      // operands of this 32-key chunk, shared by the wave's active tiles
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          kop[tt][kk] = *reinterpret_cast<const OT*>(kb + (c * 32 + 16 * tt) * 256 + koff[kk]);
-#pragma unroll
-      for (int nn = 0; nn < NN; ++nn) {
-        const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (v4i16 __attribute__((address_space(3)))*)((const lds_u8*)vb + nn * 4096 + c * 1024 + voff));
-        const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (v4i16 __attribute__((address_space(3)))*)((const lds_u8*)vb + nn * 4096 + c * 1024 + 512 + voff));
-        const u32x2 l0 = __builtin_bit_cast(u32x2, h0), l1 = __builtin_bit_cast(u32x2, h1);
-        vop[nn] = __builtin_bit_cast(OT, u32x4{l0[0], l0[1], l1[0], l1[1]});
-      }
-    }
-    if (tiles) {
-      const int kbase = kpos_blk + c * 32 + 4 * g;
-      if (tiles == 3) pf_chunk<3, OT>(w, kop, vop, bias, ones, sl2, causal, kbase);
-      else if (tiles == 1) pf_chunk<1, OT>(w, kop, vop, bias, ones, sl2, causal, kbase);
-      else pf_chunk<2, OT>(w, kop, vop, bias, ones, sl2, causal, kbase);
-    }
-  }
+  if (tiles == 3) pf_chunks<3, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  else if (tiles == 1) pf_chunks<1, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  else if (tiles == 2) pf_chunks<2, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
 }
 
 // ---- staged formats -------------------------------------------------------
@@ -294,7 +322,10 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* k
 //          (2 x 1152 B, adjacent in the page), piece q at q.
 template <int FMT>
 __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a, int kvh, int phys) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));   // recompute the lane offsets here rather than keep them live across blocks
+  phys = __builtin_amdgcn_readfirstlane(phys);
   const int64_t boff = (int64_t)phys * a.blk_units * a.sub_stride + (int64_t)kvh * a.head_stride;
   if constexpr (FMT == kFmtFp8) {
     const int rs = a.row_stride;
@@ -359,7 +390,8 @@ __device__ __forceinline__ void pf_stage_item(const uint8_t* raw, bool v_side, i
 
 template <int FMT>
 __device__ __forceinline__ void pf_stage_convert(const uint8_t* raw, uint8_t* kc, uint8_t* vc, int nkeys) {
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));    // as in the copy issue: offsets recomputed per block
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int q = k * kPfThreads + tid;
