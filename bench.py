@@ -141,6 +141,41 @@ def _read_csv(d):
     return rows
 
 
+def _counter_section(args, key):
+    """Per-dispatch medians of the SQ counters in --counter-dirs, with the
+    matrix-core busy fraction they imply."""
+    import numpy as np
+    vals = {}
+    for d in args.counter_dirs.split(","):
+        per = {}
+        for r in _read_csv(d):
+            if key in r.get("Kernel_Name", "") and "Counter_Name" in r:
+                per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+                per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for name, by_dispatch in per.items():
+            vals[name] = float(np.median(list(by_dispatch.values())))
+    out = ["", "Counters (median per dispatch; SQ wave counters count 4-cycle units):", "",
+           "| counter | value |", "|---|---|"]
+    out += [f"| {k} | {v:.4g} |" for k, v in sorted(vals.items())]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals:
+        # GRBM_GUI_ACTIVE sums the 8 XCDs; the MFMA busy count sums the 4 SIMDs of all 256 CUs
+        cycles = vals["GRBM_GUI_ACTIVE"] / 8
+        busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * 256 * 4)
+        out += ["", f"* matrix cores busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs x 4 SIMDs) "
+                f"= {100 * busy:.1f} %"]
+    if "SQ_INSTS_MFMA" in vals:
+        out += [f"* MFMA instructions: {vals['SQ_INSTS_MFMA']:.4g} x 16384 flop (16x16x32) = "
+                f"{vals['SQ_INSTS_MFMA'] * 16384 / 1e12:.3f} Tflop executed per dispatch"]
+        if "SQ_INSTS_LDS" in vals:
+            out += [f"* LDS instructions per MFMA: {vals['SQ_INSTS_LDS'] / vals['SQ_INSTS_MFMA']:.2f}"]
+        if "SQ_INSTS_VALU" in vals:
+            out += [f"* other VALU instructions per MFMA: "
+                    f"{(vals['SQ_INSTS_VALU'] - vals['SQ_INSTS_MFMA']) / vals['SQ_INSTS_MFMA']:.2f}"]
+    if "SQ_WAIT_ANY" in vals and "SQ_WAVE_CYCLES" in vals:
+        out += [f"* waves waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES): {100 * vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.1f} %"]
+    return out
+
+
 def summarize(args):
     """Write profiles/<name>.md from rocprofv3 outputs (kernel trace + two counter runs + copy calibration)."""
     import numpy as np
@@ -185,6 +220,8 @@ def summarize(args):
                       key=lambda r: -float(r["TotalDurationNs"]))[:8]
     for r in allstats:
         lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {r['Percentage']} |")
+    if args.counter_dirs:
+        lines += _counter_section(args, key)
     lines += ["", f"<!-- traffic-json: {json.dumps(info)} -->", ""]
     with open(args.out, "w") as f:
         f.write("\n".join(lines))
@@ -214,6 +251,7 @@ def main():
     ap.add_argument("--copy-fetch-dir")
     ap.add_argument("--copy-write-dir")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--counter-dirs", default="", help="comma-separated rocprofv3 --pmc outputs of SQ counters")
     ap.add_argument("--commands", default="")
     ap.add_argument("--out")
     args = ap.parse_args()
