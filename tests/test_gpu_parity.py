@@ -8,6 +8,8 @@ one of the two bf16 neighbours of the oracle value.  Every unread byte of
 the cache is NaN-poisoned.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -366,6 +368,47 @@ def test_empty_context_rows_are_zero():
     wl.topk[2] = np.array([10_000] * wl.topk_k)
     out, _ = _parity(wl)
     assert (out[1].float() == 0).all() and (out[2].float() == 0).all()
+
+
+@pytest.mark.parametrize("name,kw,strict", [
+    # top-k at the ABI's maximum, 1024 blocks: rows of up to 131072 tokens.
+    # Their outputs average 10^4 to 10^5 tokens and stay below 0.1, where a
+    # 1e-2 bound could not see a dropped block; rounding leaves ~1e-4.
+    ("C2s", dict(seq_lens=[131072 + 77, 90000], k=1024, Hq=16, Hkv=2, dql=2, seed=81), 1e-3),
+    ("C4s", dict(qlens=[40, 3], context=[131000, 5000], k=1024, Hq=16, Hkv=2, pad_rows=2, seed=82), 1e-3),
+    # a block table wider than the matrix-core kernel's 2048 columns (row-wise prefill)
+    ("C4s", dict(qlens=[9, 30], context=[270000, 100], k=16, Hq=16, Hkv=2, pad_rows=1, seed=83), None),
+])
+def test_largest_contexts(name, kw, strict):
+    _, err = _parity(make_workload(name, **kw))
+    if strict is not None:
+        assert err <= strict, f"max abs error {err}"
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s", "C4s", "C5s"])
+def test_blocks_outside_the_cache_are_skipped(name):
+    # Block-table entries that name pages outside the cache (past its end, or
+    # negative) add nothing and are never read: the output equals the
+    # oracle's with those blocks dropped from every top-k row.
+    wl = make_workload(name, seed=84)
+    cache = make_kv_cache(wl, DEV)
+    q = make_query(wl, DEV)
+    req, pos = oracle_positions(wl)
+    nblk0 = int((wl.seq_lens[0] + 127) // 128)
+    bad_logical = [b for b in (0, 2) if b < nblk0]
+    bad = dataclasses.replace(wl, block_table=wl.block_table.copy())
+    bad.block_table[0, bad_logical] = [wl.num_phys_blocks + 1000, -7][:len(bad_logical)]
+    got = _run(bad, cache, q).float().cpu().numpy()
+    topk = wl.topk.copy()
+    rows0 = np.flatnonzero(req == 0)
+    topk[rows0] = np.where(np.isin(topk[rows0], bad_logical), -1, topk[rows0])
+    assert (topk != wl.topk).any()           # some row did select a bad block
+    rows = np.arange(wl.total_q)
+    oc, bt, _, _ = compact_oracle_inputs(wl, cache, rows)
+    want = oracle.sparse_attention(q_f64(q), oc, topk, bt, req, pos, wl.softmax_scale)
+    assert np.isfinite(got).all()
+    ok, err, _ = attention_within_tolerance(got, want, ATOL)
+    assert ok, f"max abs error {err}"
 
 
 # ---------------------------------------------------------------- index cache
