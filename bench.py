@@ -228,6 +228,35 @@ def summarize(args):
     print(json.dumps(info))
 
 
+def _ceilings(torch, dev):
+    """Measured context for the datasheet fractions: what a plain device copy,
+    a plain read (a reduction) and a large bf16 GEMM reach on this GPU."""
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / 1e3 / reps
+    n = 4 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    t_read = timed(lambda: src.sum(dtype=torch.float32))
+    del dst
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    t_mm = timed(lambda: a @ b)
+    return {"ceilings": {"copy_GBs": 2 * n / t_copy / 1e9, "read_GBs": n / t_read / 1e9,
+                         "bf16_gemm_TFLOPs": 2 * m ** 3 / t_mm / 1e12,
+                         "what": "4 GiB device copy (read + write bytes), 4 GiB bf16 sum (read bytes), "
+                                 "8192^3 bf16 torch matmul"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +272,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--ceilings", action="store_true", help="measure copy / read / bf16 GEMM ceilings and exit")
     ap.add_argument("--summarize", action="store_true", help="write a profiles/ summary from rocprofv3 CSVs")
     ap.add_argument("--kernel", default="attend_rows_kernel")
     ap.add_argument("--trace-dir")
@@ -277,6 +307,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.ceilings:
+        print(json.dumps(_ceilings(torch, dev)), flush=True)
         return
     wl = make_workload(args.config, **({"kv_dtype": args.kv_dtype} if args.kv_dtype else {}))
     print(f"[bench] {workload_key(args)}: building inputs", file=sys.stderr, flush=True)
