@@ -121,6 +121,8 @@ def _need(t, name, dtype=None, dim=None, device=None):
         raise ValueError(f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if device is not None and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
     if t.dim() > 0 and t.stride(-1) != 1:
         raise ValueError(f"{name} needs a contiguous last dimension")
 
@@ -152,6 +154,15 @@ class KVCache:
         if self.layout not in _KV_LAYOUTS:
             raise ValueError(f"layout {self.layout!r}: one of {sorted(_KV_LAYOUTS)}")
         kp = self.k_pages
+        if self.layout == "page16" and kp.shape[0] > 0 and not kp[0].is_contiguous():
+            raise ValueError("each page of k_pages must be dense in memory (only the page stride is free)")
+        if self.layout == "page16" and self.v_pages is not None and self.v_pages.shape[0] > 0 \
+                and not self.v_pages[0].is_contiguous():
+            raise ValueError("each page of v_pages must be dense in memory (only the page stride is free)")
+        if kp.device.type != "cuda":
+            raise ValueError(f"k_pages must be a GPU tensor, got {kp.device}")
+        if self.v_pages is not None and self.v_pages.device != kp.device:
+            raise ValueError(f"v_pages is on {self.v_pages.device}, k_pages on {kp.device}")
         for name, s in (("k_scale", self.k_scale), ("v_scale", self.v_scale)):
             if s is not None:
                 _need(s, name, torch.float32, device=kp.device)
@@ -221,6 +232,8 @@ def msa_decode_workspace_size(total_q, num_q_heads, head_dim, topk_k):
 
 def _check_q(q, name="q"):
     _need(q, name, torch.bfloat16, 3)
+    if q.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {q.device}")
     if not q.is_contiguous():
         raise ValueError(f"{name} must be contiguous [rows, heads, head_dim]")
 
@@ -372,6 +385,8 @@ def msa_insert_index_cache(index_k, index_cache, index_slot_mapping):
     dev = index_cache.device
     if index_k.device != dev or index_slot_mapping.device != dev:
         raise ValueError("all tensors must be on one device")
+    if dev.type != "cuda":
+        raise ValueError(f"index tensors must be GPU tensors, got {dev}")
     _call("msa_insert_index_cache", _ptr(index_k), index_k.stride(0), index_k.stride(1), index_k.shape[0],
           index_k.shape[1], _ELEM[index_k.dtype], _ptr(index_cache), index_cache.stride(0), index_cache.stride(1),
           index_cache.stride(2), index_cache.shape[0], index_cache.shape[1], _ptr(index_slot_mapping),

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import block_sparse_paged_query_amd as msa
@@ -165,3 +166,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(msa, "library_path", lambda: str(tmp_path / "libmsa.so"))
     with pytest.raises(RuntimeError, match="not built"):
         msa.load_library()
+
+
+def test_binding_rejects_host_tensors():
+    # host pointers must never reach the kernels
+    import torch
+    from synth import make_workload, make_kv_cache, make_query
+    wl = make_workload("C1")
+    cache = make_kv_cache(wl, "cpu")
+    q = make_query(wl, "cpu")
+    kv = msa.KVCache(wl.kv_dtype, cache["k_pages"], cache["v_pages"], wl.num_kv_heads, wl.head_dim)
+    t = lambda x: torch.from_numpy(x)
+    with pytest.raises(ValueError, match="GPU"):
+        msa.msa_sparse_decode(q, kv, t(wl.topk), t(wl.block_table), t(wl.seq_lens), wl.softmax_scale)
+    with pytest.raises(ValueError, match="GPU"):
+        kv._struct()
+    with pytest.raises(ValueError, match="GPU"):
+        msa.msa_build_sparse_block_table(t(wl.topk), t(wl.block_table), seq_lens=t(wl.seq_lens))
+    with pytest.raises(ValueError, match="GPU"):
+        msa.msa_query_token_positions(t(np.array([0, 3], np.int32)), t(np.array([0], np.int32)), 3)
+
+
+def test_binding_rejects_pages_that_are_not_dense():
+    import torch
+    kp = torch.zeros((4, 2, 16, 256), dtype=torch.bfloat16)[..., :128]    # a head_dim slice of wider rows
+    kv = msa.KVCache("bf16", kp, kp, 2, 128)
+    with pytest.raises(ValueError, match="dense"):
+        kv._struct()
