@@ -108,7 +108,6 @@ __device__ __forceinline__ T load_or_zero(bool ok, const void* p) {
 // or past num_records bytes returns 0 and touches no memory, which masks the
 // tokens past the context and blocks outside the cache without branches.
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
-constexpr int kRawBufferWord3 = 0x00020000;   // 32-bit data format
 
 __device__ __forceinline__ BufRsrc make_rsrc(const uint8_t* p, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, bytes, kRawBufferWord3);

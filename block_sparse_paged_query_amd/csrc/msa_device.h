@@ -89,6 +89,10 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a 
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Word 3 of a raw buffer descriptor (unit stride, no swizzle, 32-bit data
+// format): a load at or past num_records bytes returns 0 and touches no memory.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // ---------------------------------------------------------------------------
 // NVFP4 slot byte order, head_dim 128 ([NV4] customize_spec leaves the bytes
 // inside a page to the kernels).  A slot holds 16 tokens: 1024 code bytes

@@ -75,16 +75,17 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // V layout: 16-byte slot ((lc / 2) * 128 + key) * 2 + lc % 2 holds chunk lc
 // (d = 8 lc .. 8 lc + 7) of key.
 
-// Piece `part` (0..3) of the copy of block `phys` (logical block `blk`), kv
-// head kvh, into LDS (kb, vb): one 16-byte K load and one V load per lane.
-// K unit (wave, part) holds keys 16 wave + 4 part + lane / 16 (one page per
-// wave), V unit holds keys 32 part + lane / 2 (two pages) at d chunk
-// 2 wave + lane % 2, so the addresses are a per-block scalar base plus a small
-// per-lane constant.  Keys at or past seq_len (only in a request's last
-// block) are read from key 0 of the block instead (finite data that gets
-// probability zero), so no NaN of an unwritten slot reaches the products.
-__device__ __forceinline__ void pf_issue_part(lds_u8* kb, lds_u8* vb, const AttendArgs& a, int kvh, int phys,
-                                              int blk, int seq_len, int part) {
+// The copy of block `phys` (logical block `blk`), kv head kvh, into LDS
+// (kb, vb): four 16-byte K loads and four V loads per lane.  K unit
+// (wave, part) holds keys 16 wave + 4 part + lane / 16 (one page per wave),
+// V unit holds keys 32 part + lane / 2 (two pages) at d chunk
+// 2 wave + lane % 2, so every address is a per-block scalar base plus a small
+// per-lane offset (V: the same offset for all four parts).  Keys at or past
+// seq_len (only in a request's last block) are read from key 0 of the block
+// instead (finite data that gets probability zero), so no NaN of an
+// unwritten slot reaches the products.
+__device__ __forceinline__ void pf_issue_block(lds_u8* kb, lds_u8* vb, const AttendArgs& a, int kvh, int phys,
+                                               int blk, int seq_len) {
   // (block ids come from LDS: make their uniformity explicit so that the
   // bases below are scalar and only 32-bit lane offsets stay in registers)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -95,23 +96,36 @@ __device__ __forceinline__ void pf_issue_part(lds_u8* kb, lds_u8* vb, const Atte
   const int64_t boff = (int64_t)phys * a.blk_units * a.sub_stride + (int64_t)kvh * a.head_stride;
   const int rs = a.row_stride;
   const int nkeys = seq_len - blk * kBlockTokens;     // keys of this block that exist (>= 1)
-  const int unit = wave * 4 + part;                   // 1 KB unit of the 32 KB block this wave fills
-  const int kkey = 16 * wave + 4 * part + (lane >> 4), kpc = lane & 15;
-  const int vkey = 32 * part + (lane >> 1), vlc = 2 * wave + (lane & 1);
-  if (nkeys >= kBlockTokens && a.sub_stride < (int64_t(1) << 30)) {
-    const uint8_t* kbase = a.k_base + boff + wave * a.sub_stride;
-    const uint8_t* vbase = a.v_base + boff + 2 * part * a.sub_stride;
-    const uint32_t koff = (uint32_t)((kkey & 15) * rs + ((kpc ^ k_swz(kkey)) << 4));
-    const uint32_t voff = (uint32_t)((lane >> 5) * a.sub_stride + (vkey & 15) * rs + (vlc << 4));
-    __builtin_amdgcn_global_load_lds(kbase + koff, kb + unit * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + voff, vb + unit * 1024, 16, 0, 0);
+  const int kq = lane >> 4, kpc = lane & 15;          // K: key 16 wave + 4 part + kq, 16-byte chunk kpc
+  const int vq = lane >> 1, vlc = 2 * wave + (lane & 1);   // V: key 32 part + vq, chunk vlc
+  if (nkeys >= kBlockTokens && a.sub_stride < (int64_t(1) << 27)) {
+    // scalar buffer descriptors over the wave's K page and the block's V
+    // pages; lanes add 32-bit offsets (V parts: a scalar offset per part)
+    const int vspan = (int)(7 * a.sub_stride) + kPageTokens * rs;
+    const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.k_base + boff + wave * a.sub_stride), (short)0, kPageTokens * rs, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr_ =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_base + boff), (short)0, vspan, kRawBufferWord3);
+    const int voff = (vq >> 4) * (int)a.sub_stride + (vq & 15) * rs + (vlc << 4);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      const int kr = 4 * part + kq;                   // key within the wave's page
+      const int koff = kr * rs + ((kpc ^ k_swz(kr)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr_, kb + (wave * 4 + part) * 1024, 16, koff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr_, vb + (wave * 4 + part) * 1024, 16, voff,
+                                               2 * part * (int)a.sub_stride, 0, 0);
+    }
   } else {
-    const int ks = kkey < nkeys ? kkey : 0, vs = vkey < nkeys ? vkey : 0;
-    __builtin_amdgcn_global_load_lds(a.k_base + boff + (ks >> 4) * a.sub_stride + (ks & 15) * rs +
-                                         ((kpc ^ k_swz(kkey)) << 4),
-                                     kb + unit * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(a.v_base + boff + (vs >> 4) * a.sub_stride + (vs & 15) * rs + (vlc << 4),
-                                     vb + unit * 1024, 16, 0, 0);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      const int kkey = 16 * wave + 4 * part + kq, vkey = 32 * part + vq;
+      const int ks = kkey < nkeys ? kkey : 0, vs = vkey < nkeys ? vkey : 0;
+      __builtin_amdgcn_global_load_lds(a.k_base + boff + (ks >> 4) * a.sub_stride + (ks & 15) * rs +
+                                           ((kpc ^ k_swz(kkey)) << 4),
+                                       kb + (wave * 4 + part) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.v_base + boff + (vs >> 4) * a.sub_stride + (vs & 15) * rs + (vlc << 4),
+                                       vb + (wave * 4 + part) * 1024, 16, 0, 0);
+    }
   }
 }
 
@@ -301,10 +315,7 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* k
   const int kpos_blk = blk * kBlockTokens;
   const uint32_t one2 = kF16 ? 0x3c003c00u : 0x3f803f80u;   // 1.0 x 2 in the operand type
   const OT ones = __builtin_bit_cast(OT, u32x4{one2, one2, one2, one2});
-  if (nx.valid) {
-#pragma unroll
-    for (int part = 0; part < 4; ++part) pf_issue_part(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len, part);
-  }
+  if (nx.valid) pf_issue_block(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len);
   if (tiles == 3) pf_chunks<3, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
   else if (tiles == 1) pf_chunks<1, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
   else if (tiles == 2) pf_chunks<2, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
@@ -327,6 +338,37 @@ __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a,
   asm volatile("" : "+v"(lane));   // recompute the lane offsets here rather than keep them live across blocks
   phys = __builtin_amdgcn_readfirstlane(phys);
   const int64_t boff = (int64_t)phys * a.blk_units * a.sub_stride + (int64_t)kvh * a.head_stride;
+  if (a.sub_stride < (int64_t(1) << 27)) {
+    // scalar buffer descriptors over the block's pages, 32-bit lane offsets
+    const int sub = (int)a.sub_stride;
+    if constexpr (FMT == kFmtFp8) {
+      const int rs = a.row_stride, span = 7 * sub + kPageTokens * rs;
+      const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_base + boff),
+                                                                           (short)0, span, kRawBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_base + boff),
+                                                                           (short)0, span, kRawBufferWord3);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int q = k * kPfThreads + wave * 64 + lane;
+        const int key = k < 2 ? q >> 3 : (q - 1024) & 127, n = k < 2 ? q & 7 : (q - 1024) >> 7;
+        const int off = (key >> 4) * sub + (key & 15) * rs + 16 * n;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k < 2 ? kr_ : vr_, raw + (k * kPfThreads + wave * 64) * 16, 16, off,
+                                                 0, 0, 0);
+      }
+    } else {
+      constexpr int SLOT = 9 * 128, PAGE_PIECES = 2 * SLOT / 16;   // 144 pieces of 16 B per page
+      const __amdgpu_buffer_rsrc_t r_ = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.k_base + boff), (short)0, 7 * sub + 2 * SLOT, kRawBufferWord3);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (k == 2 && wave >= 2) break;   // 1152 pieces: the third pass is two waves
+        const int q = k * kPfThreads + wave * 64 + lane;
+        const int page = q / PAGE_PIECES, off = page * sub + (q - page * PAGE_PIECES) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, raw + (k * kPfThreads + wave * 64) * 16, 16, off, 0, 0, 0);
+      }
+    }
+    return;
+  }
   if constexpr (FMT == kFmtFp8) {
     const int rs = a.row_stride;
 #pragma unroll
@@ -558,8 +600,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   if constexpr (FMT == kFmtBf16) {
     lds_u8 *k0 = (lds_u8*)bA, *k1 = (lds_u8*)bB, *v0 = (lds_u8*)bC, *v1 = (lds_u8*)bD;
     if (n_act > 0) {
-#pragma unroll
-      for (int part = 0; part < 4; ++part) pf_issue_part(k0, v0, a, kvh, s_phys[0], s_list[0], seq_len, part);
+      pf_issue_block(k0, v0, a, kvh, s_phys[0], s_list[0], seq_len);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
