@@ -378,9 +378,9 @@ __device__ __forceinline__ void compute_chunk(WaveState<FMT, D>& st, const Chunk
       sc[4 + i] = tok0 + 16 + i < lim ? sc[4 + i] : -INFINITY;
     }
   }
-  float mx = sc[0];
+  float mx = sc[0];   // IEEE maximum: v_maximum3, no NaN-quieting moves
 #pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+  for (int i = 1; i < 8; ++i) mx = __builtin_elementwise_maximum(mx, sc[i]);
   const float mxs = mx * sl2;
   if (__ballot(mxs > st.m + kLazyMax)) {   // rare after the first chunk
     float mh = fmaxf(mxs, __shfl_xor(mxs, 16));

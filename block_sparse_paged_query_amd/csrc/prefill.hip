@@ -193,9 +193,11 @@ __device__ __forceinline__ void pf_chunk(PfWave<OT>& w, OT (&kop)[2][PfWave<OT>:
         sv[i][ii] = kp <= w.lpos[i] ? sv[i][ii] : -INFINITY;
       }
     }
+    // (IEEE maximum: one v_maximum3 per two scores, no NaN-quieting moves;
+    // a NaN score gives a NaN probability either way)
     float mx = sv[i][0];
 #pragma unroll
-    for (int ii = 1; ii < 8; ++ii) mx = fmaxf(mx, sv[i][ii]);
+    for (int ii = 1; ii < 8; ++ii) mx = __builtin_elementwise_maximum(mx, sv[i][ii]);
     mxs[i] = fmaf(mx, sl2, bias[i]);                       // this lane's chunk max, scaled (log2 units)
     need |= mxs[i] > w.m[i] + kLazy;
   }
