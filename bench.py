@@ -105,13 +105,18 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash(mode):
+    """Hash of the code (comments and whitespace dropped) of a mode's kernel sources."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_paged_query_amd", "csrc")
     for f in KERNEL_SOURCES[mode]:
         p = os.path.join(csrc, f)
         if os.path.exists(p):
-            h.update(open(p, "rb").read())
+            text = open(p).read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -11,14 +11,14 @@
 // [SPA] vllm.models.minimax_m3.amd.ops.sparse_pa,
 //      _write_sparse_block_table_row_from_values: which tokens a row sees.
 //
-// Work decomposition.  One workgroup (W = 2..4 waves, chosen at launch so
+// Work decomposition.  One workgroup (W = 3 or 4 waves, chosen at launch so
 // that the grid fills whole rounds of the machine) owns (row, kv head,
 // split).  Wave 0 compacts the row's top-k ids into the slot list (full
 // blocks, then the causal tail) in LDS.  The row's context [0, ctx) is cut
 // into 32-token chunks (two 16-token pages of one 128-token block); a split
 // owns a contiguous range of chunks and its W waves take every W-th chunk.
 // Each wave keeps its own online-softmax state and several chunks' loads in
-// flight; the four states are merged through LDS at the end.  With one split
+// flight; the W states are merged through LDS at the end.  With one split
 // the workgroup writes the bf16 output directly; otherwise it writes an fp32
 // partial (o, m, l) and attend_merge combines.
 //
@@ -72,14 +72,14 @@ constexpr int kWavesPerSimd = FMT == kFmtNvfp4 ? 3 : 2;
 template <int FMT, int D>
 struct ChunkRaw;
 
-// bf16 pages: [page][Hkv][16][D] bf16.
+// bf16 pages: each token's D elements (16-token page tiles or K|V rows).
 template <int D>
 struct ChunkRaw<kFmtBf16, D> {
   static constexpr int KK = D / 32, NN = D / 16;
   u32x4 k[2][KK];          // tile t, step kk: one bf16x8 operand
   uint32_t v[8][NN / 2];   // row i: NN bf16 of columns r*NN ..
 };
-// fp8 pages: [page][Hkv][16][D] E4M3FN codes.
+// fp8 pages: each token's D E4M3FN codes, laid out as for bf16.
 template <int D>
 struct ChunkRaw<kFmtFp8, D> {
   static constexpr int KK = D / 32, NN = D / 16;
@@ -131,10 +131,6 @@ __device__ __forceinline__ uint32_t buf_load4(BufRsrc r, uint32_t off) {
 template <int AUX>
 __device__ __forceinline__ uint32_t buf_load2(BufRsrc r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, AUX);
-}
-template <int AUX>
-__device__ __forceinline__ uint32_t buf_load1(BufRsrc r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, AUX);
 }
 
 // Byte offsets of one lane's loads inside a page tile (bf16 / fp8: the 16
@@ -442,7 +438,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   typedef typename OpType<FMT>::type OT;
   __shared__ AttendSmem<D> sm;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int nw = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);   // waves of the workgroup (2..4)
+  const int nw = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);   // waves of the workgroup (3 or 4)
   const int r = lane & 15, g = lane >> 4;
   int bid = blockIdx.x;
   const int split = bid % a.nsplit;

@@ -15,8 +15,9 @@
 // first builds, per block of the request, the bit mask of its rows that
 // selected it (and may see it causally), then walks the blocks some row
 // selected in ascending order.  Each such block's K and V (128 keys x 256 B)
-// go once into LDS by direct global-to-LDS loads (each lane's LDS slot is
-// fixed, so layouts are made by choosing which global chunk a lane fetches),
+// go once into LDS by direct-to-LDS buffer loads (a scalar descriptor per
+// block, 32-bit lane offsets; each lane's LDS slot is fixed, so layouts are
+// made by choosing which global chunk a lane fetches),
 // double-buffered: K as [key][d] with 16-byte chunks XOR-swizzled by key, V
 // as [d pair of 16-byte chunks][key] so that the transposing read
 // ds_read_b64_tr_b16 (a lane receives one column of the 4 key rows its
