@@ -352,6 +352,31 @@ def test_mixed_batch_in_a_graph():
         assert torch.equal(out, eager), f"replay {i}"
 
 
+@pytest.mark.parametrize("name", ["C1", "C2s", "C5s"])
+def test_decode_split_counts(name):
+    # The split count follows the workspace the caller passes: the full size
+    # (as many splits as fill the machine), room for two splits, or none at
+    # all (one split, written straight to the output).  Each result matches
+    # the oracle.
+    wl = make_workload(name)
+    cache = make_kv_cache(wl, DEV)
+    q = make_query(wl, DEV)
+    kv = _kv(wl, cache)
+    topk, bt, seq = _dev(wl.topk), _dev(wl.block_table), _dev(wl.seq_lens)
+    rows = np.arange(wl.total_q)
+    req, pos = oracle_positions(wl)
+    oc, obt, _, _ = compact_oracle_inputs(wl, cache, rows)
+    want = oracle.sparse_attention(q_f64(q), oc, wl.topk, obt, req, pos, wl.softmax_scale)
+    two = wl.total_q * wl.num_q_heads * 2 * (wl.head_dim + 2) * 4 + 256
+    for ws in (None, torch.empty(two, dtype=torch.uint8, device=DEV), torch.empty(1, dtype=torch.uint8, device=DEV)):
+        out = msa.msa_sparse_decode(q, kv, topk, bt, seq, wl.softmax_scale, decode_query_len=wl.decode_query_len,
+                                    workspace=ws)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        ok, err, _ = attention_within_tolerance(got, want, ATOL)
+        assert ok, f"workspace {None if ws is None else ws.numel()}: max abs error {err}"
+
+
 def test_decode_deterministic():
     wl = make_workload("C3s")
     cache = make_kv_cache(wl, DEV)
