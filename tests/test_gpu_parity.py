@@ -176,6 +176,8 @@ def test_decode_dql_and_head_dim_variants():
     # multi-token decode at head_dim 64 with GQA 2, and bf16 at dql 3
     _parity(make_workload("C3s", D=64, Hq=16, Hkv=8, k=8, seed=31))
     _parity(make_workload("C2s", dql=3, Hq=32, Hkv=2, seed=32))
+    # NVFP4 pages, two tokens per request, 16 query heads per kv head
+    _parity(make_workload("C5s", dql=2, Hq=32, Hkv=2, seed=33))
 
 
 def test_prefill_parity_small():
