@@ -260,9 +260,15 @@ __device__ __forceinline__ void issue_loads(ChunkRaw<FMT, D>& raw, const ChunkLo
   }
 }
 
-// Compute operand type: bf16 for bf16 / fp8 pages, fp16 for NVFP4 pages.
+// Operand types.  QK^T: bf16 for bf16 / fp8 pages, fp16 for NVFP4 pages (the
+// query is converted once).  PV: fp16 wherever V is exact in fp16 (E4M3 and
+// e2m1 x E4M3 values are), so the probabilities keep 11 significant bits
+// instead of bf16's 8; bf16 pages keep bf16 V and probabilities (bf16's
+// range is wider than fp16's).
 template <int FMT> struct OpType { typedef bf16x8 type; };
 template <> struct OpType<kFmtNvfp4> { typedef f16x8 type; };
+template <int FMT> struct PvType { typedef f16x8 type; };
+template <> struct PvType<kFmtBf16> { typedef bf16x8 type; };
 
 // K operand of tile t, step kk.
 template <int FMT, int D>
@@ -309,10 +315,10 @@ __device__ __forceinline__ void v_operands(const ChunkRaw<FMT, D>& raw, u32x4 vo
         // (a0, b0, a1, b1) and (a2, b2, a3, b3)
         const uint32_t lo = (a & 0xffu) | ((b & 0xffu) << 8) | ((a & 0xff00u) << 8) | ((b & 0xff00u) << 16);
         const uint32_t hi = ((a >> 16) & 0xffu) | ((b >> 8) & 0xff00u) | ((a >> 8) & 0xff0000u) | (b & 0xff000000u);
-        vop[4 * w + 0][p] = fp8x2_to_bf16x2<false>(lo);
-        vop[4 * w + 1][p] = fp8x2_to_bf16x2<true>(lo);
-        vop[4 * w + 2][p] = fp8x2_to_bf16x2<false>(hi);
-        vop[4 * w + 3][p] = fp8x2_to_bf16x2<true>(hi);
+        vop[4 * w + 0][p] = f16x2_bits(fp8x2_to_f16x2<false>(lo));
+        vop[4 * w + 1][p] = f16x2_bits(fp8x2_to_f16x2<true>(lo));
+        vop[4 * w + 2][p] = f16x2_bits(fp8x2_to_f16x2<false>(hi));
+        vop[4 * w + 3][p] = f16x2_bits(fp8x2_to_f16x2<true>(hi));
       }
     } else {
       const uint32_t a = raw.v[2 * p], b = raw.v[2 * p + 1];
@@ -392,15 +398,16 @@ __device__ __forceinline__ void compute_chunk(WaveState<FMT, D>& st, const Chunk
   float p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(sc[i], sl2, off));
+  typedef typename PvType<FMT>::type PT;
   u32x4 pw, onesw;
-  if constexpr (FMT == kFmtNvfp4) {
+  if constexpr (FMT != kFmtBf16) {
     pw = u32x4{pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]), pack_f16(p[6], p[7])};
     onesw = u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
   } else {
     pw = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
     onesw = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   }
-  const OT pop = __builtin_bit_cast(OT, pw);
+  const PT pop = __builtin_bit_cast(PT, pw);
   u32x4 vop[NN];
   if constexpr (FMT == kFmtNvfp4) {
     ChunkRaw<FMT, D> rv = raw;
@@ -418,8 +425,8 @@ __device__ __forceinline__ void compute_chunk(WaveState<FMT, D>& st, const Chunk
     v_operands<FMT, D>(raw, vop);
   }
 #pragma unroll
-  for (int nn = 0; nn < NN; ++nn) st.acc[nn] = mfma16(__builtin_bit_cast(OT, vop[nn]), pop, st.acc[nn]);
-  st.lacc = mfma16(__builtin_bit_cast(OT, onesw), pop, st.lacc);
+  for (int nn = 0; nn < NN; ++nn) st.acc[nn] = mfma16(__builtin_bit_cast(PT, vop[nn]), pop, st.acc[nn]);
+  st.lacc = mfma16(__builtin_bit_cast(PT, onesw), pop, st.lacc);
 }
 
 // Shared memory of one workgroup.

@@ -57,6 +57,10 @@ constexpr int kPfRawBytes = FMT == kFmtBf16 ? kPfBlockBytes : (FMT == kFmtFp8 ? 
 // compute operand type: bf16 for bf16 / fp8 pages, fp16 for NVFP4 pages
 template <int FMT> struct PfOp { typedef bf16x8 type; };
 template <> struct PfOp<kFmtNvfp4> { typedef f16x8 type; };
+// PV operand type: fp16 wherever V is exact in fp16 (E4M3, e2m1 x E4M3), so
+// the probabilities keep 11 significant bits; bf16 pages stay bf16
+template <int FMT> struct PfPv { typedef f16x8 type; };
+template <> struct PfPv<kFmtBf16> { typedef bf16x8 type; };
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -158,12 +162,12 @@ constexpr float kLazy = 8.f;
 // chunk's once this chunk's products have consumed them, so those LDS reads
 // overlap this chunk's softmax and PV work instead of stalling the next
 // chunk's first product.
-template <int MASK, class OT, class NextK, class NextV>
-__device__ __forceinline__ void pf_chunk(PfWave<OT>& w, OT (&kop)[2][PfWave<OT>::KK], OT (&vop)[PfWave<OT>::NN],
-                                         const float (&bias)[kPfTiles], const OT& ones, float sl2, bool causal,
+template <int MASK, class OT, class PT, class NextK, class NextV>
+__device__ __forceinline__ void pf_chunk(PfWave<OT>& w, OT (&kop)[2][PfWave<OT>::KK], PT (&vop)[PfWave<OT>::NN],
+                                         const float (&bias)[kPfTiles], const PT& ones, float sl2, bool causal,
                                          int kbase, NextK&& next_k, NextV&& next_v) {
   constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
-  constexpr bool kF16 = __is_same(OT, f16x8);
+  constexpr bool kF16 = __is_same(PT, f16x8);
   float sv[kPfTiles][8];
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
@@ -229,7 +233,7 @@ __device__ __forceinline__ void pf_chunk(PfWave<OT>& w, OT (&kop)[2][PfWave<OT>:
     } else {
       pw = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
     }
-    const OT pop = __builtin_bit_cast(OT, pw);
+    const PT pop = __builtin_bit_cast(PT, pw);
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = mfma16(vop[nn], pop, w.acc[i][nn]);
     w.lacc[i] = mfma16(ones, pop, w.lacc[i]);
@@ -248,10 +252,10 @@ struct PfNext {       // the block whose copies are issued during this one
 // The block's four 32-key chunks against the tiles in MASK.  Each chunk's K
 // and V operands (shared by the wave's active tiles) are read from LDS while
 // the previous chunk computes.
-template <int MASK, class OT>
+template <int MASK, class OT, class PT>
 __device__ __forceinline__ void pf_chunks(PfWave<OT>& w, const uint8_t* kb, const uint8_t* vb,
                                           const int (&koff)[PfWave<OT>::KK], int voff,
-                                          const float (&bias)[kPfTiles], const OT& ones, float sl2, bool causal,
+                                          const float (&bias)[kPfTiles], const PT& ones, float sl2, bool causal,
                                           int kbase0) {
   constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
   auto load_k = [&](OT (&kop)[2][KK], int c) {
@@ -261,7 +265,7 @@ __device__ __forceinline__ void pf_chunks(PfWave<OT>& w, const uint8_t* kb, cons
       for (int kk = 0; kk < KK; ++kk)
         kop[tt][kk] = *reinterpret_cast<const OT*>(kb + (c * 32 + 16 * tt) * 256 + koff[kk]);
   };
-  auto load_v = [&](OT (&vop)[NN], int c) {
+  auto load_v = [&](PT (&vop)[NN], int c) {
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) {
       const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -269,18 +273,18 @@ __device__ __forceinline__ void pf_chunks(PfWave<OT>& w, const uint8_t* kb, cons
       const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (v4i16 __attribute__((address_space(3)))*)((const lds_u8*)vb + nn * 4096 + c * 1024 + 512 + voff));
       const u32x2 l0 = __builtin_bit_cast(u32x2, h0), l1 = __builtin_bit_cast(u32x2, h1);
-      vop[nn] = __builtin_bit_cast(OT, u32x4{l0[0], l0[1], l1[0], l1[1]});
+      vop[nn] = __builtin_bit_cast(PT, u32x4{l0[0], l0[1], l1[0], l1[1]});
     }
   };
   OT kop[2][KK];
-  OT vop[NN];
+  PT vop[NN];
   load_k(kop, 0);
   load_v(vop, 0);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    pf_chunk<MASK, OT>(w, kop, vop, bias, ones, sl2, causal, kbase0 + c * 32,
+    pf_chunk<MASK, OT, PT>(w, kop, vop, bias, ones, sl2, causal, kbase0 + c * 32,
                        [&](OT (&k)[2][KK]) { if (c < 3) load_k(k, c + 1); },
-                       [&](OT (&v)[NN]) { if (c < 3) load_v(v, c + 1); });
+                       [&](PT (&v)[NN]) { if (c < 3) load_v(v, c + 1); });
   }
 }
 
@@ -289,12 +293,12 @@ __device__ __forceinline__ void pf_chunks(PfWave<OT>& w, const uint8_t* kb, cons
 // position must be masked); earlier blocks need only the row selection.
 // Every wave first issues its pieces of the next block's copies, active or
 // not.
-template <class OT>
+template <class OT, class PT>
 __device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* kb, const uint8_t* vb, uint32_t bmask,
                                                  int blk, int wave, int RT, float sl2, bool causal,
                                                  const PfNext& nx, const AttendArgs& a, int kvh, int seq_len) {
   constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
-  constexpr bool kF16 = __is_same(OT, f16x8);
+  constexpr bool kF16 = __is_same(PT, f16x8);
   static_assert(kPfTiles == 2, "the tile sets below enumerate two tiles");
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   // per-lane LDS offsets (chunk / tile / step parts are compile-time)
@@ -317,11 +321,11 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* k
   }
   const int kpos_blk = blk * kBlockTokens;
   const uint32_t one2 = kF16 ? 0x3c003c00u : 0x3f803f80u;   // 1.0 x 2 in the operand type
-  const OT ones = __builtin_bit_cast(OT, u32x4{one2, one2, one2, one2});
+  const PT ones = __builtin_bit_cast(PT, u32x4{one2, one2, one2, one2});
   if (nx.valid) pf_issue_block(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len);
-  if (tiles == 3) pf_chunks<3, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
-  else if (tiles == 1) pf_chunks<1, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
-  else if (tiles == 2) pf_chunks<2, OT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  if (tiles == 3) pf_chunks<3, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  else if (tiles == 1) pf_chunks<1, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  else if (tiles == 2) pf_chunks<2, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
 }
 
 // ---- staged formats -------------------------------------------------------
@@ -408,11 +412,12 @@ __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a,
 template <int FMT>
 __device__ __forceinline__ void pf_stage_item(const uint8_t* raw, bool v_side, int key, int n, uint32_t out[8]) {
   if constexpr (FMT == kFmtFp8) {
+    // K -> bf16 (the QK^T operand type), V -> fp16 (the PV operand type)
     const u32x4 w = *reinterpret_cast<const u32x4*>(raw + (v_side ? 16384 + (n * 128 + key) * 16 : key * 128 + 16 * n));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[2 * i] = fp8x2_to_bf16x2<false>(w[i]);
-      out[2 * i + 1] = fp8x2_to_bf16x2<true>(w[i]);
+      out[2 * i] = v_side ? f16x2_bits(fp8x2_to_f16x2<false>(w[i])) : fp8x2_to_bf16x2<false>(w[i]);
+      out[2 * i + 1] = v_side ? f16x2_bits(fp8x2_to_f16x2<true>(w[i])) : fp8x2_to_bf16x2<true>(w[i]);
     }
   } else {
     const uint8_t* slot = raw + (key >> 4) * (2 * kNvfp4SlotBytes) + (v_side ? kNvfp4SlotBytes : 0);
@@ -464,6 +469,7 @@ __device__ __forceinline__ void pf_stage_convert(const uint8_t* raw, uint8_t* kc
 template <int FMT>
 __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const AttendArgs a, int n_slots) {
   typedef typename PfOp<FMT>::type OT;
+  typedef typename PfPv<FMT>::type PT;
   constexpr int D = 128, KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
   // Four LDS buffers as distinct objects: the loops below are unrolled by two,
   // so the compiler knows the in-flight copies target another buffer.
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
         const PfNext nx = {k1, v1, it + 1 < n_act ? s_phys[it + 1] : 0, it + 1 < n_act ? (int)s_list[it + 1] : 0,
                            it + 1 < n_act};
         const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-        pf_compute_block<OT>(w, bA, bC, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
+        pf_compute_block<OT, PT>(w, bA, bC, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
         __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
         __syncthreads();
       }
@@ -625,7 +631,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
         const PfNext nx = {k0, v0, it + 2 < n_act ? s_phys[it + 2] : 0, it + 2 < n_act ? (int)s_list[it + 2] : 0,
                            it + 2 < n_act};
         const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-        pf_compute_block<OT>(w, bB, bD, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
+        pf_compute_block<OT, PT>(w, bB, bD, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
@@ -643,7 +649,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
         __syncthreads();
         if (it + 1 < n_act) pf_stage_issue<FMT>((lds_u8*)bD, a, kvh, s_phys[it + 1]);
         const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-        pf_compute_block<OT>(w, bA, bB, bmask, j, wave, RT, sl2, j >= own_first, none, a, kvh, seq_len);
+        pf_compute_block<OT, PT>(w, bA, bB, bmask, j, wave, RT, sl2, j >= own_first, none, a, kvh, seq_len);
         __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
         __syncthreads();                 // and every wave is done with (bA, bB)
       }
@@ -654,7 +660,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
         __syncthreads();
         if (it + 2 < n_act) pf_stage_issue<FMT>((lds_u8*)bC, a, kvh, s_phys[it + 2]);
         const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-        pf_compute_block<OT>(w, bA, bB, bmask, j, wave, RT, sl2, j >= own_first, none, a, kvh, seq_len);
+        pf_compute_block<OT, PT>(w, bA, bB, bmask, j, wave, RT, sl2, j >= own_first, none, a, kvh, seq_len);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }

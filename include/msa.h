@@ -201,8 +201,9 @@ MSA_API size_t msa_decode_workspace_size(int32_t total_q, int32_t num_q_heads, i
  * table lookup as in msa_build_sparse_block_table (decode mode).
  * out = softmax(softmax_scale * k_scale * q K^T over the row's tokens) V
  *       * v_scale, with K, V the stored codes; a row with no tokens gets 0.
- * Compute: bf16 (fp16 for NVFP4, where e2m1 x E4M3 products are exact)
- * matrix-core inputs, fp32 accumulation and softmax, output rounded to
+ * Compute: matrix-core inputs in bf16 for q K^T (fp16 for NVFP4, where
+ * e2m1 x E4M3 products are exact) and in fp16 for P V on fp8 / NVFP4 pages
+ * (bf16 on bf16 pages); fp32 accumulation and softmax; output rounded to
  * nearest even.
  * topk_k <= 1024; head_dim 64 or 128 (NVFP4: 128);
  * num_q_heads / num_kv_heads <= 16.
