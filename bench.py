@@ -404,7 +404,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": f"{workload_key(args)} {describe(args)}", "rows": wl.total_q,
-                   "sum_ctx": sum_ctx, "kernel_ms": kernel_ms, "layers": len(layers)},
+                   "sum_ctx": sum_ctx, "kernel_ms": kernel_ms, "layers": len(layers),
+                   "tokens_per_s": wl.total_q / (ms_per_step * 1e-3)},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
