@@ -13,7 +13,9 @@ pages in the 256 MB last-level cache.
 Prints one JSON line.  value = algorithmic work of a step / wall time per step
 over the K timed steps; roofline.achieved = the same work / the average kernel
 time of a step from HIP events on the launch stream (one pair around the
-timed steps); cpu_baseline = the fp64
+timed steps); config.call_ms_median / call_ms_min = the median and the
+fastest of the same number of single calls timed one by one after the timed
+region (an event pair around each); cpu_baseline = the fp64
 CPU oracle timed on a bounded sample of the same workload.
 """
 
@@ -391,6 +393,15 @@ def main():
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
+    # spread of single calls: the same steps again, an event pair around each
+    # (after the timed region, so its figures are not affected)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(pairs):
+        e0.record()
+        step(i)
+        e1.record()
+    torch.cuda.synchronize()
+    call_ms = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
     if wl.mode == "decode":
         value, unit = work / (ms_per_step * 1e-3) / 1e9, "GB/s"
         achieved = work / (kernel_ms * 1e-3) / 1e9
@@ -412,7 +423,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": f"{workload_key(args)} {describe(args)}", "rows": wl.total_q,
-                   "sum_ctx": sum_ctx, "kernel_ms": kernel_ms, "layers": len(layers),
+                   "sum_ctx": sum_ctx, "kernel_ms": kernel_ms, "call_ms_median": call_ms[len(call_ms) // 2],
+                   "call_ms_min": call_ms[0], "layers": len(layers),
                    "tokens_per_s": wl.total_q / (ms_per_step * 1e-3)},
         "roofline": roof, "cpu_baseline": cpu,
     }
