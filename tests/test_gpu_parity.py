@@ -222,6 +222,19 @@ def test_prefill_parity_full_size_sampled(kv_dtype):
     _parity(wl, rows)
 
 
+@pytest.mark.parametrize("name,cols", [("C4s", 2050), ("C4s:fp8", 2050), ("C2s", 4100)])
+def test_wide_block_table(name, cols):
+    # a block table wider than the matrix-core prefill indexes (2048 columns)
+    # sends prefill to the row-wise kernel; the added columns are never named
+    # by a row's top-k ids and hold block 0
+    name, _, dt = name.partition(":")
+    wl = make_workload(name, seed=61, **({"kv_dtype": dt} if dt else {}))
+    cache = make_kv_cache(wl, DEV)
+    extra = np.zeros((wl.block_table.shape[0], cols - wl.block_table.shape[1]), np.int32)
+    wl = dataclasses.replace(wl, block_table=np.concatenate([wl.block_table, extra], 1))
+    _parity(wl, cache=cache)
+
+
 def _block_outer(cache, layers=3, layer=1):
     """The same pages re-homed in a block-outer buffer of `layers` layers:
     page p of this layer at (p * layers + layer) * page bytes, the other
