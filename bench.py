@@ -50,7 +50,8 @@ DESCR = {
 def workload_key(args):
     """Config name, with the page format when --kv-dtype overrides it."""
     return (args.config + (f"/{args.kv_dtype}" if args.kv_dtype else "")
-            + ("/rows128" if args.layout == "rows128" else ""))
+            + ("/rows128" if args.layout == "rows128" else "")
+            + ("/per-block-selection" if args.selection == "per_block" else ""))
 
 
 def describe(args):
@@ -59,6 +60,8 @@ def describe(args):
         d = d.replace("bf16", args.kv_dtype).replace("fp8 e4m3", args.kv_dtype).replace("NVFP4", args.kv_dtype)
     if args.layout == "rows128":
         d += ", 128-token pages with K|V-interleaved rows"
+    if args.selection == "per_block":
+        d += ", rows sharing a 128-token block share one top-k draw (variant, not the named workload)"
     return d
 
 
@@ -280,6 +283,8 @@ def main():
     ap.add_argument("--config", default="C2", choices=sorted(DESCR))
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8", "nvfp4"], default=None,
                     help="page format instead of the workload's own (fp8 / NVFP4 prefill)")
+    ap.add_argument("--selection", choices=["independent", "per_block"], default="independent",
+                    help="top-k draws: one per row (the named workloads) or one per request and 128-token block")
     ap.add_argument("--layout", choices=["page16", "rows128"], default="page16",
                     help="cache layout (rows128: bf16 / fp8 only)")
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated across steps")
@@ -326,7 +331,8 @@ def main():
     if args.ceilings:
         print(json.dumps(_ceilings(torch, dev)), flush=True)
         return
-    wl = make_workload(args.config, **({"kv_dtype": args.kv_dtype} if args.kv_dtype else {}))
+    wl = make_workload(args.config, selection=args.selection,
+                       **({"kv_dtype": args.kv_dtype} if args.kv_dtype else {}))
     print(f"[bench] {workload_key(args)}: building inputs", file=sys.stderr, flush=True)
     cache = make_kv_cache(wl, dev)
     if args.layout == "rows128":

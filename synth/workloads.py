@@ -108,8 +108,15 @@ def _draw_row(rng, own_blk, k):
     return row
 
 
-def make_workload(name, *, block_page_stride=8, seed=None, **overrides):
-    """Build the metadata of a named workload (numpy, seeded)."""
+def make_workload(name, *, block_page_stride=8, seed=None, selection="independent", **overrides):
+    """Build the metadata of a named workload (numpy, seeded).
+
+    selection: "independent" (every row draws its own earlier blocks, the
+    named workloads) or "per_block" (the rows of a request whose positions
+    share a 128-token block share one draw; a variant for measurement only,
+    with the same context lengths)."""
+    if selection not in ("independent", "per_block"):
+        raise ValueError(f"selection {selection!r}")
     cfg = dict(CONFIGS[name])
     cfg.update(overrides)
     seed = cfg["seed"] if seed is None else seed
@@ -147,8 +154,14 @@ def make_workload(name, *, block_page_stride=8, seed=None, **overrides):
         bt[r, :n] = perm[off:off + n]
         off += n
     topk = np.full((total_q, k), -1, dtype=np.int64)
+    shared = {}
     for i in range(total_q):
-        if i < n_real:
+        if i < n_real and selection == "per_block":
+            key = (int(row_req[i]), int(row_pos[i]) // BLOCK)
+            if key not in shared:
+                shared[key] = _draw_row(rng, key[1], k)
+            topk[i] = shared[key]
+        elif i < n_real:
             topk[i] = _draw_row(rng, int(row_pos[i]) // BLOCK, k)
         else:
             topk[i] = rng.choice(max_blocks, size=min(k, max_blocks), replace=False).tolist() + [-1] * (k - min(k, max_blocks))

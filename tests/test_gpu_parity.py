@@ -201,6 +201,7 @@ def test_prefill_parity_small():
     dict(kv_dtype="fp8", qlens=[0, 300], context=[50, 0], seed=54),
     dict(kv_dtype="fp8", Hq=16, Hkv=4, seed=52),         # 4 per kv head: row-wise path
     dict(kv_dtype="nvfp4", Hq=16, Hkv=4, seed=55),       # 4 per kv head: row-wise path
+    dict(selection="per_block", seed=56),                # rows of one block share their top-k row
 ])
 def test_prefill_parity_variants(kw):
     _parity(make_workload("C4s", **kw))
