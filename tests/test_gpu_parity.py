@@ -402,6 +402,26 @@ def test_decode_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "nvfp4"])
+def test_prefill_deterministic(kv_dtype):
+    wl = make_workload("C4s", kv_dtype=kv_dtype)
+    cache = make_kv_cache(wl, DEV)
+    q = make_query(wl, DEV)
+    a = _run(wl, cache, q)
+    b = _run(wl, cache, q)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_prefill_many_small_requests(kv_dtype):
+    # 150 requests of 0 to 6 new tokens after 0 to 3000 tokens of context:
+    # tiles hold one request's rows only, so most of them are mostly empty
+    rng = np.random.default_rng(91)
+    qlens = rng.integers(0, 7, size=150).tolist()
+    context = rng.integers(0, 3001, size=150).tolist()
+    _parity(make_workload("C4s", kv_dtype=kv_dtype, qlens=qlens, context=context, pad_rows=3, seed=92))
+
+
 def test_empty_context_rows_are_zero():
     # a decode row whose every id is in the future or padding attends nothing
     wl = make_workload("C2s")
