@@ -21,10 +21,17 @@ method is described on, cited by page title and section:
 
 Floating point is fp64 throughout.  Each function is pinned by a CPU test
 under ``tests/`` against something other than itself (worked examples,
-closed forms, library routines, brute force); the two conventions the pages
-leave open and that no pin can fix are marked "parity unpinned" where they
-are defined (the GQA head grouping is pinned to torch's ``enable_gqa``
-convention; the NVFP4 in-page byte order is ours).
+closed forms, library routines, brute force).  Two conventions the pages
+leave open cannot be pinned and are marked "parity unpinned" where they are
+defined:
+
+* parity unpinned: the NVFP4 in-page byte order (``nvfp4_token_values``), a
+  layout of ours; only the quantise -> dequantise error bound checks it;
+* parity unpinned: the zero output of a row with an empty context
+  (``attend_row``).
+
+The grouped-query head mapping is a reading too, but it is pinned to torch's
+``enable_gqa`` convention.
 """
 
 from .msa_oracle import *  # noqa: F401,F403

@@ -350,7 +350,9 @@ def attend_row(q_row, K, V, softmax_scale):
     q_row [Hq, D]; K, V [n, Hkv, D].  Reading (grouped-query attention, the
     pages do not print the mapping): q head h reads kv head h // (Hq / Hkv),
     torch's enable_gqa convention.  An empty context gives a zero output
-    (reading: nothing to average).
+    (reading: nothing to average).  PARITY UNPINNED for that zero: the pages
+    print no output for an empty context, so it is a convention (the kernels
+    follow the same one).
     """
     Hq, D = q_row.shape
     n, Hkv, _ = K.shape
