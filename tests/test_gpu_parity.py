@@ -236,6 +236,44 @@ def test_wide_block_table(name, cols):
     _parity(wl, cache=cache)
 
 
+def _sweep_cases(n=24, seed=2024):
+    """Seeded random small shapes across modes, page formats, head groups,
+    head dims, top-k widths, block page strides and layouts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        mode = "decode" if i % 2 == 0 else "prefill"
+        dt = ["bf16", "fp8", "nvfp4"][int(rng.integers(3))]
+        D = 128 if dt == "nvfp4" else int(rng.choice([64, 128, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8, 8, 16, 16]))   # 8 and 16 take the matrix-core prefill
+        k = int(rng.choice([1, 2, 5, 16, 33]))
+        stride = int(rng.choice([8, 16]))
+        rows128 = dt != "nvfp4" and stride == 8 and rng.random() < 0.3
+        kw = dict(kv_dtype=dt, D=D, Hq=Hkv * G, Hkv=Hkv, k=k, seed=300 + i)
+        if mode == "decode":
+            dql = int(rng.integers(1, 5))
+            kw.update(seq_lens=rng.integers(dql, 4000, size=int(rng.integers(1, 6))).tolist(), dql=dql)
+            name = "C1"
+        else:
+            nreq = int(rng.integers(1, 4))
+            kw.update(qlens=rng.integers(0, 120, size=nreq).tolist(), context=rng.integers(0, 3000, size=nreq).tolist(),
+                      pad_rows=int(rng.integers(0, 4)))
+            name = "C4s"
+        tag = f"{mode}-{dt}-D{D}-Hkv{Hkv}-G{G}-k{k}-s{stride}" + ("-rows128" if rows128 else "")
+        cases.append(pytest.param(name, kw, stride, rows128, id=tag))
+    return cases
+
+
+@pytest.mark.parametrize("name,kw,stride,rows128", _sweep_cases())
+def test_random_shapes_sweep(name, kw, stride, rows128):
+    wl = make_workload(name, block_page_stride=stride, **kw)
+    cache = make_kv_cache(wl, DEV)
+    if rows128:
+        cache = rows128_cache(cache, wl)
+    _parity(wl, cache=cache)
+
+
 def _block_outer(cache, layers=3, layer=1):
     """The same pages re-homed in a block-outer buffer of `layers` layers:
     page p of this layer at (p * layers + layer) * page bytes, the other
