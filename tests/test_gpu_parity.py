@@ -216,9 +216,10 @@ def test_decode_parity_full_size_sampled(name, rows):
     _parity(make_workload(name), rows)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "nvfp4"])
-def test_prefill_parity_full_size_sampled(kv_dtype):
-    wl = make_workload("C4", kv_dtype=kv_dtype)
+@pytest.mark.parametrize("kv_dtype,selection", [("bf16", "independent"), ("fp8", "independent"),
+                                                ("nvfp4", "independent"), ("bf16", "per_block")])
+def test_prefill_parity_full_size_sampled(kv_dtype, selection):
+    wl = make_workload("C4", kv_dtype=kv_dtype, selection=selection)
     rows = [0, 127, 128, 2047, 2048, 6000, 14335, 14336, 22527, 22528, 22591]
     _parity(wl, rows)
 
