@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
 * ``msa_sparse_prefill``           - block-sparse ragged causal prefill
 * ``msa_insert_index_cache``       - index-key side-cache scatter
 * ``msa_debug_dequant_tokens``     - test hook: dequantized K/V of tokens
+* ``msa_debug_read_probe``         - measurement hook: a plain read of 4 KB chunks
 """
 
 from __future__ import annotations
@@ -28,7 +29,7 @@ __all__ = [
     "MsaError", "KVCache", "library_path", "load_library",
     "msa_build_sparse_block_table", "msa_query_token_positions",
     "msa_sparse_decode", "msa_sparse_prefill", "msa_sparse_attention", "msa_insert_index_cache",
-    "msa_debug_dequant_tokens", "msa_decode_workspace_size",
+    "msa_debug_dequant_tokens", "msa_debug_read_probe", "msa_decode_workspace_size",
     "MSA_BF16", "MSA_FP16", "MSA_FP8_E4M3FN", "MSA_NVFP4", "MSA_FP32",
 ]
 
@@ -77,6 +78,7 @@ _SIGS = {
     "msa_insert_index_cache": ([_P, _I64, _I64, _I32, _I32, _I32, _P, _I64, _I64, _I64, _I32, _I32, _P, _I64,
                                 _P], _I32),
     "msa_debug_dequant_tokens": ([ctypes.POINTER(_KV), _P, _P, _I32, _P, _P, _P], _I32),
+    "msa_debug_read_probe": ([_P, ctypes.c_uint32, _P, _P, _SZ, _P], _I32),
 }
 _lib = None
 
@@ -404,3 +406,25 @@ def msa_debug_dequant_tokens(kv: KVCache, pages, slots):
     kvs = kv._struct()
     _call("msa_debug_dequant_tokens", ctypes.byref(kvs), _ptr(pages), _ptr(slots), n, _ptr(k), _ptr(v), _stream(dev))
     return k, v
+
+
+def msa_debug_read_probe(buf, order=None, out=None):
+    """Read ``buf`` (a contiguous GPU tensor of a whole number of 4096-byte
+    chunks) chunk by chunk, in ``order`` (int32 chunk ids on the same device;
+    None = in address order), and return the [4096 * 256] int32 checksum
+    words.  A measurement hook: time it to see what a plain read reaches."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if nbytes % 4096:
+        raise ValueError(f"buf holds {nbytes} bytes, not a whole number of 4096-byte chunks")
+    n = nbytes // 4096
+    if order is not None:
+        _need(order, "order", torch.int32, 1, buf.device)
+        if order.shape[0] != n:
+            raise ValueError(f"order has {order.shape[0]} entries, buf {n} chunks")
+    if out is None:
+        out = torch.empty(4096 * 256, dtype=torch.int32, device=buf.device)
+    _need(out, "out", torch.int32, 1, buf.device)
+    _call("msa_debug_read_probe", _ptr(buf), n, _ptr(order), _ptr(out), out.numel(), _stream(buf.device))
+    return out

@@ -240,6 +240,12 @@ int choose_splits(int64_t rows, int32_t num_kv_heads, int32_t topk_k, int cus) {
 
 }  // namespace
 
+namespace msa {
+extern const int kReadProbeBlocks;   // read_probe.hip
+hipError_t launch_read_probe(const void* buf, const uint32_t* order, uint32_t n_chunks, uint32_t* out,
+                             hipStream_t stream);
+}  // namespace msa
+
 extern "C" {
 
 MSA_API const char* msa_last_error(void) { return g_last_error; }
@@ -509,6 +515,16 @@ MSA_API msa_status_t msa_debug_dequant_tokens(const msa_kv_cache_t* kv, const in
   a.k_out = k_out;
   a.v_out = v_out;
   return hip_status(msa::launch_debug_dequant(a, stream), "dequant hook launch");
+}
+
+MSA_API msa_status_t msa_debug_read_probe(const void* buf, uint32_t n_chunks, const uint32_t* order, uint32_t* out,
+                                          size_t out_words, hipStream_t stream) {
+  MSA_CHECK(out_words >= (size_t)msa::kReadProbeBlocks * 256, MSA_ERR_INVALID_ARGUMENT,
+            "out holds %zu words, the probe writes %d", out_words, msa::kReadProbeBlocks * 256);
+  MSA_CHECK(out != nullptr, MSA_ERR_INVALID_ARGUMENT, "out is NULL");
+  MSA_CHECK(n_chunks == 0 || (buf != nullptr && (reinterpret_cast<uintptr_t>(buf) & 15) == 0),
+            MSA_ERR_INVALID_ARGUMENT, "buf must be non-NULL and 16-byte aligned");
+  return hip_status(msa::launch_read_probe(buf, order, n_chunks, out, stream), "read probe launch");
 }
 
 }  // extern "C"

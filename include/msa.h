@@ -301,6 +301,18 @@ MSA_API msa_status_t msa_debug_dequant_tokens(
     const msa_kv_cache_t* kv, const int32_t* pages, const int32_t* slots, int32_t n,
     float* k_out, float* v_out, hipStream_t stream);
 
+/*
+ * Measurement hook: a plain read of n_chunks 4096-byte chunks of buf, in
+ * the order order[0 .. n_chunks) (chunk ids; NULL = 0, 1, 2, ...; ids at or
+ * past n_chunks read nothing), with the 16-byte non-temporal loads the
+ * decode's page reads use.  Not part of attention: it times what the GPU's
+ * memory delivers to a kernel that only reads.  out receives 1048576 uint32
+ * checksum words (4096 workgroups x 256 threads); out_words must be at least
+ * that.  buf holds at least n_chunks * 4096 bytes, 16-byte aligned.
+ */
+MSA_API msa_status_t msa_debug_read_probe(const void* buf, uint32_t n_chunks, const uint32_t* order, uint32_t* out,
+                                          size_t out_words, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -193,3 +193,12 @@ def test_binding_rejects_pages_that_are_not_dense():
     kv = msa.KVCache("bf16", kp, kp, 2, 128)
     with pytest.raises(ValueError, match="dense"):
         kv._struct()
+
+
+def test_read_probe_argument_errors():
+    lib = _lib()
+    assert lib.msa_debug_read_probe(FAKE, 4, None, FAKE, 1000, None) == 1          # out too small
+    assert lib.msa_debug_read_probe(ctypes.c_void_p(0x1008), 4, None, FAKE, 1 << 20, None) == 1   # misaligned
+    assert lib.msa_debug_read_probe(None, 4, None, FAKE, 1 << 20, None) == 1       # NULL buffer
+    assert lib.msa_debug_read_probe(FAKE, 4, None, None, 1 << 20, None) == 1       # NULL out
+

@@ -525,3 +525,21 @@ def test_index_cache_insert_bit_exact():
     msa.msa_insert_index_cache(k.to(DEV), gc, slots.to(DEV))
     torch.cuda.synchronize()
     assert (gc.float().cpu().numpy() == want).all()
+
+
+def test_read_probe_reads_every_chunk_once():
+    # the XOR of all checksum words is the XOR of every 32-bit word read, so
+    # any order of the 64 chunks gives the XOR of the whole buffer; an id
+    # past the end reads nothing, which drops its chunk from the XOR
+    g = torch.Generator(device="cpu").manual_seed(3)
+    host = torch.randint(0, 2 ** 31 - 1, (64, 1024), dtype=torch.int32, generator=g)
+    buf = host.reshape(-1).to(DEV)
+    xor = lambda a: int(np.bitwise_xor.reduce(np.ascontiguousarray(a).view(np.uint32).reshape(-1)))
+    fold = lambda w: xor(w.cpu().numpy())
+    want = xor(host.numpy())
+    assert fold(msa.msa_debug_read_probe(buf)) == want
+    order = torch.randperm(64, generator=g).to(torch.int32)
+    assert fold(msa.msa_debug_read_probe(buf, order.to(DEV))) == want
+    lost = int(order[5])
+    order[5] = 1000
+    assert fold(msa.msa_debug_read_probe(buf, order.to(DEV))) == want ^ xor(host[lost].numpy())
