@@ -248,8 +248,7 @@ def summarize(args):
 
 def _ceilings(torch, dev):
     """Measured context for the datasheet fractions: what a plain device copy,
-    a plain read (a torch reduction, and the library's read probe) and a large
-    bf16 GEMM reach on this GPU."""
+    a plain read (a torch reduction) and a large bf16 GEMM reach on this GPU."""
     def timed(fn, reps=10):
         fn()
         torch.cuda.synchronize()
@@ -266,27 +265,14 @@ def _ceilings(torch, dev):
     t_copy = timed(lambda: dst.copy_(src))
     t_read = timed(lambda: src.sum(dtype=torch.float32))
     del dst
-    # the library's read probe: 4 KB chunks with the decode's 16-byte loads,
-    # in address order and in a seeded random order
-    import block_sparse_paged_query_amd as msa
-    chunks = n // 4096
-    gen = torch.Generator(device="cpu").manual_seed(7)
-    order = torch.randperm(chunks, generator=gen).to(device=dev, dtype=torch.int32)
-    words = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
-    t_probe_seq = timed(lambda: msa.msa_debug_read_probe(src, None, words))
-    t_probe_rand = timed(lambda: msa.msa_debug_read_probe(src, order, words))
-    del order, words
     m = 8192
     a = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
     b = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
     t_mm = timed(lambda: a @ b)
     return {"ceilings": {"copy_GBs": 2 * n / t_copy / 1e9, "read_GBs": n / t_read / 1e9,
-                         "probe_read_in_order_GBs": n / t_probe_seq / 1e9,
-                         "probe_read_random_4KB_GBs": n / t_probe_rand / 1e9,
                          "bf16_gemm_TFLOPs": 2 * m ** 3 / t_mm / 1e12,
                          "what": "4 GiB device copy (read + write bytes), 4 GiB bf16 sum (read bytes), "
-                                 "msa_debug_read_probe over the same 4 GiB in address order and in a random "
-                                 "order of 4 KB chunks (read bytes), 8192^3 bf16 torch matmul"}}
+                                 "8192^3 bf16 torch matmul"}}
 
 
 def main():

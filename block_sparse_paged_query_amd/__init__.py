@@ -14,7 +14,6 @@ Entry points (same names as the C ABI):
 * ``msa_sparse_prefill``           - block-sparse ragged causal prefill
 * ``msa_insert_index_cache``       - index-key side-cache scatter
 * ``msa_debug_dequant_tokens``     - test hook: dequantized K/V of tokens
-* ``msa_debug_read_probe``         - measurement hook: a plain read of 4 KB chunks
 """
 
 from __future__ import annotations
@@ -29,7 +28,7 @@ __all__ = [
     "MsaError", "KVCache", "library_path", "load_library",
     "msa_build_sparse_block_table", "msa_query_token_positions",
     "msa_sparse_decode", "msa_sparse_prefill", "msa_sparse_attention", "msa_insert_index_cache",
-    "msa_debug_dequant_tokens", "msa_debug_read_probe", "msa_decode_workspace_size",
+    "msa_debug_dequant_tokens", "msa_decode_workspace_size",
     "MSA_BF16", "MSA_FP16", "MSA_FP8_E4M3FN", "MSA_NVFP4", "MSA_FP32",
 ]
 
@@ -78,7 +77,6 @@ _SIGS = {
     "msa_insert_index_cache": ([_P, _I64, _I64, _I32, _I32, _I32, _P, _I64, _I64, _I64, _I32, _I32, _P, _I64,
                                 _P], _I32),
     "msa_debug_dequant_tokens": ([ctypes.POINTER(_KV), _P, _P, _I32, _P, _P, _P], _I32),
-    "msa_debug_read_probe": ([_P, ctypes.c_uint32, _P, _P, _SZ, _P], _I32),
 }
 _lib = None
 
@@ -127,6 +125,13 @@ def _need(t, name, dtype=None, dim=None, device=None):
         raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
     if t.dim() > 0 and t.stride(-1) != 1:
         raise ValueError(f"{name} needs a contiguous last dimension")
+
+
+def _need_table_rows(block_table, num_reqs, name):
+    """The kernels read row r of the block table for every request r: a
+    shorter table would be read past its end on the device."""
+    if block_table.shape[0] < num_reqs:
+        raise ValueError(f"{name} has {block_table.shape[0]} rows for {num_reqs} requests")
 
 
 @dataclasses.dataclass
@@ -194,6 +199,13 @@ def msa_build_sparse_block_table(topk, block_table, *, seq_lens=None, decode_que
     """
     if topk.dim() == 3:
         topk = topk[0]
+    if query_req_id is None:
+        # decode mode: the kernel takes block_table's row count as the request
+        # count and reads seq_lens[r] for each of them
+        if seq_lens is None:
+            raise ValueError("decode-mode tables need seq_lens (or query_req_id / query_abs_pos for prefill)")
+        if seq_lens.shape[0] != block_table.shape[0]:
+            raise ValueError(f"seq_lens has {seq_lens.shape[0]} requests, block_table {block_table.shape[0]} rows")
     dev = topk.device
     _need(topk, "topk", torch.int32, 2)
     _need(block_table, "block_table", torch.int32, 2, dev)
@@ -245,6 +257,7 @@ def msa_sparse_decode(q, kv: KVCache, topk, block_table, seq_lens, softmax_scale
     """Block-sparse GQA decode; q/out [batch * decode_query_len, Hq, D] bf16."""
     if topk.dim() == 3:
         topk = topk[0]
+    _need_table_rows(block_table, seq_lens.shape[0], "block_table")
     dev = q.device
     _check_q(q)
     _need(topk, "topk", torch.int32, 2, dev)
@@ -280,6 +293,7 @@ def msa_sparse_prefill(q, kv: KVCache, topk, block_table, cu_seqlens_q, seq_lens
     """Block-sparse ragged causal prefill; q/out [total_q, Hq, D] bf16 (padded rows -> 0)."""
     if topk.dim() == 3:
         topk = topk[0]
+    _need_table_rows(block_table, seq_lens.shape[0], "block_table")
     dev = q.device
     _check_q(q)
     _need(topk, "topk", torch.int32, 2, dev)
@@ -317,6 +331,11 @@ def msa_sparse_attention(q, kv: KVCache, topk, num_decode_tokens, softmax_scale,
     """
     if topk.dim() == 3:
         topk = topk[0]
+    nd = int(num_decode_tokens)
+    if nd > 0 and decode_block_table is not None and decode_seq_lens is not None:
+        _need_table_rows(decode_block_table, decode_seq_lens.shape[0], "decode_block_table")
+    if nd < q.shape[0] and prefill_block_table is not None and prefill_seq_lens is not None:
+        _need_table_rows(prefill_block_table, prefill_seq_lens.shape[0], "prefill_block_table")
     dev = q.device
     _check_q(q)
     _need(topk, "topk", torch.int32, 2, dev)
@@ -330,7 +349,6 @@ def msa_sparse_attention(q, kv: KVCache, topk, num_decode_tokens, softmax_scale,
         raise ValueError(f"topk has {topk.shape[0]} rows, q has {num_tokens}")
     if d != kv.head_dim:
         raise ValueError(f"q head_dim {d} != cache head_dim {kv.head_dim}")
-    nd = int(num_decode_tokens)
     if not 0 <= nd <= num_tokens:
         raise ValueError(f"num_decode_tokens {nd} of {num_tokens} rows")
     dbt = dsl = pbt = pcu = psl = None
@@ -369,28 +387,29 @@ _ELEM = {torch.bfloat16: MSA_BF16, torch.float16: MSA_FP16, torch.float32: MSA_F
 
 
 def msa_insert_index_cache(index_k, index_cache, index_slot_mapping):
-    """Scatter index keys [N, D] into the key-only cache [B, T, D] by slot (in place)."""
+    """Scatter index keys [N, D] into the key-only cache [B, T, D] by slot (in place).
+
+    Nothing is done when either tensor is empty.  The three tensors share a
+    GPU; keys and cache share one of bf16 / fp16 / fp32 / fp8 E4M3FN; the
+    slots are int64, one per key; the cache's key dimension is contiguous.
+    """
     if index_k.numel() == 0 or index_cache.numel() == 0:
         return
-    if index_k.dim() != 2 or index_cache.dim() != 3:
-        raise ValueError("index cache insert expects [N,D] and [B,T,D]")
-    if index_k.shape[1] != index_cache.shape[2]:
-        raise ValueError("index key dim must match index cache head dim")
-    if index_slot_mapping.dim() != 1 or index_slot_mapping.shape[0] != index_k.shape[0]:
-        raise ValueError("index slot mapping must be a length-N vector")
-    if index_cache.stride(2) != 1:
-        raise ValueError("index cache requires contiguous head dimension")
-    if index_k.dtype != index_cache.dtype or index_k.dtype not in _ELEM:
-        raise TypeError("index_k and index_cache must share one of bf16 / fp16 / fp32 / fp8 dtypes")
-    if index_slot_mapping.dtype != torch.int64:
-        raise TypeError("index slot mapping must be int64")
+    _need(index_cache, "index_cache", dim=3)
+    _need(index_k, "index_k", index_cache.dtype, 2)
+    _need(index_slot_mapping, "index_slot_mapping", torch.int64, 1)
+    if index_cache.dtype not in _ELEM:
+        raise TypeError(f"index_cache dtype {index_cache.dtype}: bf16, fp16, fp32 or float8_e4m3fn")
+    n, d = index_k.shape
+    if d != index_cache.shape[2]:
+        raise ValueError(f"index_k rows hold {d} elements, index_cache rows {index_cache.shape[2]}")
+    if index_slot_mapping.shape[0] != n:
+        raise ValueError(f"{index_slot_mapping.shape[0]} slots for {n} keys")
     dev = index_cache.device
-    if index_k.device != dev or index_slot_mapping.device != dev:
-        raise ValueError("all tensors must be on one device")
-    if dev.type != "cuda":
-        raise ValueError(f"index tensors must be GPU tensors, got {dev}")
-    _call("msa_insert_index_cache", _ptr(index_k), index_k.stride(0), index_k.stride(1), index_k.shape[0],
-          index_k.shape[1], _ELEM[index_k.dtype], _ptr(index_cache), index_cache.stride(0), index_cache.stride(1),
+    for t, name in ((index_cache, "index_cache"), (index_k, "index_k"), (index_slot_mapping, "index_slot_mapping")):
+        _need(t, name, device=dev)
+    _call("msa_insert_index_cache", _ptr(index_k), index_k.stride(0), index_k.stride(1), n, d,
+          _ELEM[index_k.dtype], _ptr(index_cache), index_cache.stride(0), index_cache.stride(1),
           index_cache.stride(2), index_cache.shape[0], index_cache.shape[1], _ptr(index_slot_mapping),
           index_slot_mapping.stride(0), _stream(dev))
 
@@ -406,25 +425,3 @@ def msa_debug_dequant_tokens(kv: KVCache, pages, slots):
     kvs = kv._struct()
     _call("msa_debug_dequant_tokens", ctypes.byref(kvs), _ptr(pages), _ptr(slots), n, _ptr(k), _ptr(v), _stream(dev))
     return k, v
-
-
-def msa_debug_read_probe(buf, order=None, out=None):
-    """Read ``buf`` (a contiguous GPU tensor of a whole number of 4096-byte
-    chunks) chunk by chunk, in ``order`` (int32 chunk ids on the same device;
-    None = in address order), and return the [4096 * 256] int32 checksum
-    words.  A measurement hook: time it to see what a plain read reaches."""
-    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
-        raise ValueError("buf must be a contiguous GPU tensor")
-    nbytes = buf.numel() * buf.element_size()
-    if nbytes % 4096:
-        raise ValueError(f"buf holds {nbytes} bytes, not a whole number of 4096-byte chunks")
-    n = nbytes // 4096
-    if order is not None:
-        _need(order, "order", torch.int32, 1, buf.device)
-        if order.shape[0] != n:
-            raise ValueError(f"order has {order.shape[0]} entries, buf {n} chunks")
-    if out is None:
-        out = torch.empty(4096 * 256, dtype=torch.int32, device=buf.device)
-    _need(out, "out", torch.int32, 1, buf.device)
-    _call("msa_debug_read_probe", _ptr(buf), n, _ptr(order), _ptr(out), out.numel(), _stream(buf.device))
-    return out

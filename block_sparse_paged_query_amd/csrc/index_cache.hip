@@ -1,8 +1,8 @@
 // Index-key side cache insert.
 //
 // [SPA] vllm.models.minimax_m3.amd.ops.sparse_pa, minimax_m3_insert_index_cache:
-// keys [N, D] are scattered into a key-only cache [B, T, D] through a length-N
-// slot mapping.  Slot s addresses block s / T, position s % T; negative slots
+// keys [N, D] are scattered into a key-only cache [B, T, D], one int64 slot
+// per key.  Slot s addresses block s / T, position s % T; negative slots
 // (padding) and slots past the cache are skipped.  One thread per element.
 #include "msa_device.h"
 #include "msa_internal.h"

@@ -240,12 +240,6 @@ int choose_splits(int64_t rows, int32_t num_kv_heads, int32_t topk_k, int cus) {
 
 }  // namespace
 
-namespace msa {
-extern const int kReadProbeBlocks;   // read_probe.hip
-hipError_t launch_read_probe(const void* buf, const uint32_t* order, uint32_t n_chunks, uint32_t* out,
-                             hipStream_t stream);
-}  // namespace msa
-
 extern "C" {
 
 MSA_API const char* msa_last_error(void) { return g_last_error; }
@@ -272,7 +266,7 @@ MSA_API msa_status_t msa_build_sparse_block_table(const int32_t* topk, int64_t t
   if (query_req_id == nullptr) {
     MSA_CHECK(decode_query_len >= 1, MSA_ERR_INVALID_ARGUMENT, "decode_query_len %d < 1", decode_query_len);
     MSA_CHECK((int64_t)total_q == (int64_t)num_reqs * decode_query_len, MSA_ERR_INVALID_ARGUMENT,
-              "decode top-k rows must equal batch * decode_query_len: %d != %d * %d", total_q, num_reqs,
+              "decode mode: %d top-k rows for %d requests of %d tokens each", total_q, num_reqs,
               decode_query_len);
   }
   if (total_q == 0) return ok();
@@ -461,7 +455,7 @@ MSA_API msa_status_t msa_insert_index_cache(const void* index_k, int64_t k_strid
   MSA_CHECK(n >= 0 && d >= 0 && num_blocks >= 0 && cache_block_size >= 0, MSA_ERR_INVALID_ARGUMENT,
             "negative size (n %d, d %d, blocks %d, block size %d)", n, d, num_blocks, cache_block_size);
   if (n == 0 || d == 0 || num_blocks == 0 || cache_block_size == 0) return ok();
-  MSA_CHECK(c_stride2 == 1, MSA_ERR_INVALID_ARGUMENT, "index cache requires contiguous head dimension");
+  MSA_CHECK(c_stride2 == 1, MSA_ERR_INVALID_ARGUMENT, "index cache: element stride %lld along the key dimension, 1 needed", (long long)c_stride2);
   int esize = 0;
   switch (dtype) {
     case MSA_BF16:
@@ -515,16 +509,6 @@ MSA_API msa_status_t msa_debug_dequant_tokens(const msa_kv_cache_t* kv, const in
   a.k_out = k_out;
   a.v_out = v_out;
   return hip_status(msa::launch_debug_dequant(a, stream), "dequant hook launch");
-}
-
-MSA_API msa_status_t msa_debug_read_probe(const void* buf, uint32_t n_chunks, const uint32_t* order, uint32_t* out,
-                                          size_t out_words, hipStream_t stream) {
-  MSA_CHECK(out_words >= (size_t)msa::kReadProbeBlocks * 256, MSA_ERR_INVALID_ARGUMENT,
-            "out holds %zu words, the probe writes %d", out_words, msa::kReadProbeBlocks * 256);
-  MSA_CHECK(out != nullptr, MSA_ERR_INVALID_ARGUMENT, "out is NULL");
-  MSA_CHECK(n_chunks == 0 || (buf != nullptr && (reinterpret_cast<uintptr_t>(buf) & 15) == 0),
-            MSA_ERR_INVALID_ARGUMENT, "buf must be non-NULL and 16-byte aligned");
-  return hip_status(msa::launch_read_probe(buf, order, n_chunks, out, stream), "read probe launch");
 }
 
 }  // extern "C"

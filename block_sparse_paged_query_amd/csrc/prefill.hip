@@ -506,18 +506,28 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
       running += __shfl(incl, 63);
     }
     if (lane == 0) {
-      const int real_end = a.cu_seqlens_q[R];
+      // rows outside [cu[0], cu[R]) are padding; every range is clamped to
+      // [0, total_rows), so offsets past the buffers are never formed
+      const int total = a.total_rows;
+      const int head_end = min(max(a.cu_seqlens_q[0], 0), total);
+      const int real_end = min(max(a.cu_seqlens_q[R], head_end), total);
       if (found_req >= 0) {
         s_info[0] = 0;
         s_info[1] = found_req;
-        s_info[2] = found_row0;
-        s_info[3] = min(found_row0 + QT, a.cu_seqlens_q[found_req + 1]);
+        s_info[2] = min(max(found_row0, 0), total);
+        s_info[3] = min(min(found_row0 + QT, a.cu_seqlens_q[found_req + 1]), total);
       } else {
-        const int p = t - running;   // padding tiles follow the real ones
+        // padding tiles follow the real ones: rows [0, cu[0]), then [cu[R], total)
+        const int p = t - running, n_head = (head_end + QT - 1) / QT;
         s_info[0] = 1;
         s_info[1] = 0;
-        s_info[2] = real_end + p * QT;
-        s_info[3] = min(real_end + (p + 1) * QT, a.total_rows);
+        if (p < n_head) {
+          s_info[2] = p * QT;
+          s_info[3] = min((p + 1) * QT, head_end);
+        } else {
+          s_info[2] = real_end + (p - n_head) * QT;
+          s_info[3] = min(real_end + (p - n_head + 1) * QT, total);
+        }
       }
     }
   }
@@ -688,7 +698,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
 
 hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t stream) {
   const int QT = kPfWaves * kPfTiles * (16 / a.group);
-  const int n_slots = (a.total_rows + QT - 1) / QT + a.num_reqs + 1;
+  // tiles: ceil(rows / QT) per request and per padding range (before the
+  // first request, after the last) is at most ceil(total / QT) + R + 2
+  const int n_slots = (a.total_rows + QT - 1) / QT + a.num_reqs + 2;
   const int64_t blocks = (int64_t)n_slots * a.num_kv_heads;
   if (fmt == kFmtBf16) {
     hipLaunchKernelGGL(prefill_blocks_kernel<kFmtBf16>, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a, n_slots);

@@ -108,7 +108,8 @@ typedef enum msa_kv_layout {
  * k_scale / v_scale: device fp32 scalars (NULL = 1.0).  fp8: the
  *   per-tensor dequant multipliers; NVFP4: the per-tensor global scales.
  *   They fold exactly into the softmax scale and the output scale
- *   ([FI] forward: logits are linear in K, the output in V).
+ *   ([FI] forward: a per-tensor K descale multiplies every logit and a
+ *   per-tensor V descale every output, so both move out of the kernel's inner loop).
  * num_pages: pages each buffer holds (MSA_KV_ROWS128: 128-token pages).
  *   Blocks whose pages fall outside [0, num_pages) are skipped (they add
  *   nothing), so a bad table cannot make the attend read out of bounds.
@@ -231,8 +232,10 @@ MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, 
  * q, out [total_q][num_q_heads][head_dim] bf16, contiguous.  Rows
  * cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 are request r's new tokens, at
  * positions seq_lens[r] - (cu_seqlens_q[r+1] - cu_seqlens_q[r]) + local
- * offset (seq_lens counts the new tokens); rows >= cu_seqlens_q[num_reqs]
- * are padding and get 0.  Same math, page formats and limits as
+ * offset (seq_lens counts the new tokens); rows before cu_seqlens_q[0] and
+ * rows >= cu_seqlens_q[num_reqs] are padding and get 0.  cu_seqlens_q must
+ * be non-decreasing; rows it names at or past total_q are not computed.
+ * Same math, page formats and limits as
  * msa_sparse_decode (bf16, fp8 e4m3fn or NVFP4 pages; NVFP4 computes in
  * fp16).
  */
@@ -277,7 +280,7 @@ MSA_API msa_status_t msa_sparse_attention(
 /*
  * Scatter index keys into the key-only side cache.
  * [SPA] minimax_m3_insert_index_cache: keys [N, D] into a cache [B, T, D]
- * through a length-N slot mapping; empty input returns at once; the cache's
+ * through one int64 slot per key; empty input returns at once; the cache's
  * last dimension must be contiguous.  Slot s (int64) goes to block s / T,
  * position s % T; negative slots (padding) and slots >= B*T are skipped.
  * dtype gives the element size (MSA_BF16 / MSA_FP16: 2 bytes, MSA_FP32: 4,
@@ -300,18 +303,6 @@ MSA_API msa_status_t msa_insert_index_cache(
 MSA_API msa_status_t msa_debug_dequant_tokens(
     const msa_kv_cache_t* kv, const int32_t* pages, const int32_t* slots, int32_t n,
     float* k_out, float* v_out, hipStream_t stream);
-
-/*
- * Measurement hook: a plain read of n_chunks 4096-byte chunks of buf, in
- * the order order[0 .. n_chunks) (chunk ids; NULL = 0, 1, 2, ...; ids at or
- * past n_chunks read nothing), with the 16-byte non-temporal loads the
- * decode's page reads use.  Not part of attention: it times what the GPU's
- * memory delivers to a kernel that only reads.  out receives 1048576 uint32
- * checksum words (4096 workgroups x 256 threads); out_words must be at least
- * that.  buf holds at least n_chunks * 4096 bytes, 16-byte aligned.
- */
-MSA_API msa_status_t msa_debug_read_probe(const void* buf, uint32_t n_chunks, const uint32_t* order, uint32_t* out,
-                                          size_t out_words, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -398,7 +398,7 @@ def insert_index_cache(index_k, index_cache, slot_mapping):
     """Scatter index keys into the key-only side cache, in place.
 
     [SPA] minimax_m3_insert_index_cache: keys [N, D] go into a cache
-    [B, T, D] through a length-N slot mapping; nothing happens on empty
+    [B, T, D], one int64 slot per key; nothing happens on empty
     input.  The kernel body is not printed; reading: slot s addresses block
     s // T, position s % T (the usual vLLM slot numbering), and negative
     slots (padding) are skipped.

@@ -51,9 +51,9 @@ def _table(**kw):
 
 
 def test_table_rejects_row_count_mismatch():
-    # the decode builder's assertion: rows must equal batch * decode_query_len
+    # decode-mode tables need one top-k row per (request, query token)
     assert _table(total_q=3, num_reqs=2, dql=1) == 1     # MSA_ERR_INVALID_ARGUMENT
-    assert b"batch * decode_query_len" in _lib().msa_last_error()
+    assert b"top-k rows for" in _lib().msa_last_error()
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -71,7 +71,7 @@ def test_empty_inputs_are_noops():
 
 def test_index_cache_needs_contiguous_head_dim():
     st = _lib().msa_insert_index_cache(FAKE, 128, 1, 5, 128, 0, FAKE, 128 * 16, 128, 2, 4, 16, FAKE, 1, None)
-    assert st == 1 and b"contiguous head dimension" in _lib().msa_last_error()
+    assert st == 1 and b"along the key dimension, 1 needed" in _lib().msa_last_error()
 
 
 def _kv(**kw):
@@ -195,10 +195,56 @@ def test_binding_rejects_pages_that_are_not_dense():
         kv._struct()
 
 
-def test_read_probe_argument_errors():
-    lib = _lib()
-    assert lib.msa_debug_read_probe(FAKE, 4, None, FAKE, 1000, None) == 1          # out too small
-    assert lib.msa_debug_read_probe(ctypes.c_void_p(0x1008), 4, None, FAKE, 1 << 20, None) == 1   # misaligned
-    assert lib.msa_debug_read_probe(None, 4, None, FAKE, 1 << 20, None) == 1       # NULL buffer
-    assert lib.msa_debug_read_probe(FAKE, 4, None, None, 1 << 20, None) == 1       # NULL out
+def test_binding_rejects_short_block_tables():
+    # the kernels read block_table row r for every request r (and the decode
+    # table builder seq_lens[r] for every block_table row): shapes that would
+    # send them past a buffer's end are refused before any device check
+    import torch
+    from synth import make_workload
+    wl = make_workload("C2s")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))
+    topk, bt, seq = t(wl.topk), t(wl.block_table), t(wl.seq_lens)
+    q = torch.zeros((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16)
+    kv = msa.KVCache("bf16", torch.zeros((8, 8, 16, 128), dtype=torch.bfloat16), None, 8, 128)
+    with pytest.raises(ValueError, match="rows for 3 requests"):
+        msa.msa_sparse_decode(q, kv, topk, bt[:2], seq, wl.softmax_scale)
+    with pytest.raises(ValueError, match="requests, block_table"):
+        msa.msa_build_sparse_block_table(topk, bt, seq_lens=seq[:2])
+    with pytest.raises(ValueError, match="need seq_lens"):
+        msa.msa_build_sparse_block_table(topk, bt)
+    pre = make_workload("C4s")
+    cu, pseq = t(pre.cu_seqlens_q), t(pre.seq_lens)
+    qp = torch.zeros((pre.total_q, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="rows for 2 requests"):
+        msa.msa_sparse_prefill(qp, kv, t(pre.topk), t(pre.block_table)[:1], cu, pseq, pre.softmax_scale)
+    both = torch.cat([q, qp])
+    with pytest.raises(ValueError, match="decode_block_table has 2 rows"):
+        msa.msa_sparse_attention(both, kv, t(np.concatenate([wl.topk, pre.topk])), wl.total_q, 0.1,
+                                 decode_block_table=bt[:2], decode_seq_lens=seq,
+                                 prefill_block_table=t(pre.block_table), prefill_cu_seqlens_q=cu,
+                                 prefill_seq_lens=pseq)
+    with pytest.raises(ValueError, match="prefill_block_table has 1 rows"):
+        msa.msa_sparse_attention(both, kv, t(np.concatenate([wl.topk, pre.topk])), wl.total_q, 0.1,
+                                 decode_block_table=bt, decode_seq_lens=seq,
+                                 prefill_block_table=t(pre.block_table)[:1], prefill_cu_seqlens_q=cu,
+                                 prefill_seq_lens=pseq)
 
+
+def test_index_cache_binding_checks():
+    import torch
+    k = torch.zeros((4, 8), dtype=torch.bfloat16)
+    c = torch.zeros((2, 4, 8), dtype=torch.bfloat16)
+    s = torch.zeros(4, dtype=torch.int64)
+    msa.msa_insert_index_cache(k[:0], c, s[:0])                   # empty input: nothing to do
+    with pytest.raises(ValueError, match="3-D"):
+        msa.msa_insert_index_cache(k, c[0], s)
+    with pytest.raises(ValueError, match="elements"):
+        msa.msa_insert_index_cache(torch.zeros((4, 6), dtype=torch.bfloat16), c, s)
+    with pytest.raises(ValueError, match="slots for"):
+        msa.msa_insert_index_cache(k, c, s[:3])
+    with pytest.raises(TypeError, match="int64"):
+        msa.msa_insert_index_cache(k, c, s.int())
+    with pytest.raises(ValueError, match="contiguous last"):
+        msa.msa_insert_index_cache(k, torch.zeros((2, 8, 4), dtype=torch.bfloat16).transpose(1, 2), s)
+    with pytest.raises(ValueError, match="GPU"):
+        msa.msa_insert_index_cache(k, c, s)                           # host tensors never reach a kernel

@@ -3,9 +3,9 @@
 Bit-exact: sparse block table, context lengths, prefill positions, dequant
 hook, index-cache insert.  Attention: max |GPU - oracle| <= 1e-2 (the bound
 the method's acceptance states for bf16 outputs on N(0, 1) inputs) wherever
-|oracle| < 4; above, where bf16 values are 1/32 apart, the output must be
-one of the two bf16 neighbours of the oracle value.  Every unread byte of
-the cache is NaN-poisoned.
+|oracle| < 4; above, where bf16 values are 1/32 apart, 1e-2 plus half a bf16
+spacing (the output's own rounding).  Every unread byte of the cache is
+NaN-poisoned.
 """
 
 import dataclasses
@@ -157,8 +157,9 @@ def _parity(wl, rows=None, cache=None):
     want = oracle.sparse_attention(qf, oc, wl.topk, bt, req, pos, wl.softmax_scale, rows=rows)
     got = out.float().cpu().numpy()[rows]
     assert np.isfinite(got).all()
-    ok, err, n_big = attention_within_tolerance(got, want, ATOL)
-    assert ok, f"max abs error {err} (|want| < 4), {n_big} elements checked for faithful rounding"
+    ok, err, n_big, big_ratio = attention_within_tolerance(got, want, ATOL)
+    assert ok, (f"max abs error {err} (|want| < 4); {n_big} elements with |want| >= 4 held to 1e-2 + half a bf16 "
+                f"spacing, worst at {big_ratio:.3f} of that bound")
     return out, err
 
 
@@ -428,7 +429,7 @@ def test_decode_split_counts(name):
                                     workspace=ws)
         torch.cuda.synchronize()
         got = out.float().cpu().numpy()
-        ok, err, _ = attention_within_tolerance(got, want, ATOL)
+        ok, err, _, _ = attention_within_tolerance(got, want, ATOL)
         assert ok, f"workspace {None if ws is None else ws.numel()}: max abs error {err}"
 
 
@@ -507,7 +508,7 @@ def test_blocks_outside_the_cache_are_skipped(name):
     oc, bt, _, _ = compact_oracle_inputs(wl, cache, rows)
     want = oracle.sparse_attention(q_f64(q), oc, topk, bt, req, pos, wl.softmax_scale)
     assert np.isfinite(got).all()
-    ok, err, _ = attention_within_tolerance(got, want, ATOL)
+    ok, err, _, _ = attention_within_tolerance(got, want, ATOL)
     assert ok, f"max abs error {err}"
 
 
@@ -527,19 +528,22 @@ def test_index_cache_insert_bit_exact():
     assert (gc.float().cpu().numpy() == want).all()
 
 
-def test_read_probe_reads_every_chunk_once():
-    # the XOR of all checksum words is the XOR of every 32-bit word read, so
-    # any order of the 64 chunks gives the XOR of the whole buffer; an id
-    # past the end reads nothing, which drops its chunk from the XOR
-    g = torch.Generator(device="cpu").manual_seed(3)
-    host = torch.randint(0, 2 ** 31 - 1, (64, 1024), dtype=torch.int32, generator=g)
-    buf = host.reshape(-1).to(DEV)
-    xor = lambda a: int(np.bitwise_xor.reduce(np.ascontiguousarray(a).view(np.uint32).reshape(-1)))
-    fold = lambda w: xor(w.cpu().numpy())
-    want = xor(host.numpy())
-    assert fold(msa.msa_debug_read_probe(buf)) == want
-    order = torch.randperm(64, generator=g).to(torch.int32)
-    assert fold(msa.msa_debug_read_probe(buf, order.to(DEV))) == want
-    lost = int(order[5])
-    order[5] = 1000
-    assert fold(msa.msa_debug_read_probe(buf, order.to(DEV))) == want ^ xor(host[lost].numpy())
+@pytest.mark.parametrize("kw", [dict(), dict(Hq=16, Hkv=4), dict(kv_dtype="fp8")])
+def test_prefill_rows_before_first_request(kw):
+    # cu_seqlens_q[0] > 0: the rows before the first request are padding and
+    # come out 0, on the matrix-core kernel (8 heads per kv head) and on the
+    # row-wise kernel (4 per kv head) alike; the cache is the unshifted one
+    wl = make_workload("C4s", seed=57, **kw)
+    cache = make_kv_cache(wl, DEV)
+    lead = 37
+    rng = np.random.default_rng(57)
+    cols = wl.block_table.shape[1]
+    junk = np.full((lead, wl.topk_k), -1, np.int32)      # random in-range ids, which must be dropped
+    for i in range(lead):
+        junk[i, :min(cols, wl.topk_k)] = rng.permutation(cols)[:wl.topk_k]
+    shifted = dataclasses.replace(
+        wl, cu_seqlens_q=(wl.cu_seqlens_q + lead).astype(np.int32), total_q=wl.total_q + lead,
+        topk=np.concatenate([junk, wl.topk]), gen_row_req=np.concatenate([np.zeros(lead, np.int64), wl.gen_row_req]),
+        gen_row_pos=np.concatenate([np.full(lead, -1, np.int64), wl.gen_row_pos]))
+    out, _ = _parity(shifted, cache=cache)
+    assert (out[:lead].float() == 0).all()

@@ -182,7 +182,8 @@ def test_padded_rows_are_zero():
 
 
 def test_fp8_scale_folding_identity():
-    # [FI] forward: logits are linear in K and the output in V, so
+    # [FI] forward: a K descale multiplies each logit and a V descale each
+    # output, so the two scales move out of the attention:
     # attn(q, s_k K, s_v V, tau) == s_v * attn(q, K, V, tau * s_k)
     rng = np.random.default_rng(11)
     q_row = rng.standard_normal((8, 16))
