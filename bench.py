@@ -17,6 +17,12 @@ timed steps); config.call_ms_median / call_ms_min = the median and the
 fastest of the same number of single calls timed one by one after the timed
 region (an event pair around each); cpu_baseline = the fp64
 CPU oracle timed on a bounded sample of the same workload.
+
+The default run (C2) also times C3 (fp8 multi-token decode), C4 (bf16
+prefill) and C5 (NVFP4 decode) in the same process, the same way, and lists
+them under config.also, each with its own value, unit and roofline
+(--also picks other workloads, e.g. C4/fp8 for the C4 shapes on fp8 pages;
+--also "" times the main workload only).
 """
 
 from __future__ import annotations
@@ -290,6 +296,9 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", default=None,
+                    help="other workloads timed after the main one, comma-separated (e.g. C3,C4,C5,C4/fp8); "
+                         "default: C3,C4,C5 when the main one is the default C2, else none")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--ceilings", action="store_true", help="measure copy / read / bf16 GEMM ceilings and exit")
@@ -308,15 +317,17 @@ def main():
     if args.summarize:
         summarize(args)
         return
+    if args.also is None:
+        default_main = args.config == "C2" and not args.kv_dtype and args.layout == "page16" \
+            and args.selection == "independent"
+        args.also = "C3,C4,C5" if default_main else ""
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import block_sparse_paged_query_amd as msa
-    from synth import make_kv_cache, make_query, make_workload, rows128_cache
 
     dev = "cuda"
     if args.copy_probe:
@@ -331,6 +342,45 @@ def main():
     if args.ceilings:
         print(json.dumps(_ceilings(torch, dev)), flush=True)
         return
+    primary = measure(args, torch, msa, dev, keep_inputs=not args.no_cpu_baseline)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        wl, cache, q, ctx = primary.pop("_inputs")
+        cpu = _cpu_baseline(wl, cache, q, ctx, args.cpu_seconds)
+        del wl, cache, q
+    primary.pop("_inputs", None)
+    torch.cuda.empty_cache()
+    # the other named workloads, timed the same way in the same process
+    also = []
+    for name in [c for c in args.also.split(",") if c]:
+        cfg, _, kvd = name.partition("/")
+        sub = argparse.Namespace(**vars(args))
+        sub.config, sub.kv_dtype, sub.layout, sub.selection = cfg, (kvd or None), "page16", "independent"
+        res = measure(sub, torch, msa, dev, keep_inputs=False)
+        res.pop("_inputs", None)
+        also.append({"workload": res["config"]["workload"], "value": res["value"], "unit": res["unit"],
+                     "ms_per_step": res["ms_per_step"], "kernel_ms": res["config"]["kernel_ms"],
+                     "call_ms_median": res["config"]["call_ms_median"], "call_ms_min": res["config"]["call_ms_min"],
+                     "sum_ctx": res["config"]["sum_ctx"], "tokens_per_s": res["config"]["tokens_per_s"],
+                     "dtype": res["dtype"], "roofline": res["roofline"]})
+        torch.cuda.empty_cache()
+    line = {
+        "metric": METRIC, "value": primary["value"], "unit": primary["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": primary["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": primary["dtype"], "data": "synthetic",
+        "config": dict(primary["config"], also=also),
+        "roofline": primary["roofline"], "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def measure(args, torch, msa, dev, keep_inputs):
+    """Build one workload's inputs on the GPU, time K steps after W warm-up
+    steps, and return the bench fields of that workload."""
+    import numpy as np
+    from synth import make_kv_cache, make_query, make_workload, rows128_cache
+
     wl = make_workload(args.config, selection=args.selection,
                        **({"kv_dtype": args.kv_dtype} if args.kv_dtype else {}))
     print(f"[bench] {workload_key(args)}: building inputs", file=sys.stderr, flush=True)
@@ -420,21 +470,14 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(workload_key(args), "prefill")}
         dtype = "f16" if wl.kv_dtype == "nvfp4" else "bf16"
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = _cpu_baseline(wl, cache, q, ctx, args.cpu_seconds)
-    line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
-        "config": {"workload": f"{workload_key(args)} {describe(args)}", "rows": wl.total_q,
-                   "sum_ctx": sum_ctx, "kernel_ms": kernel_ms, "call_ms_median": call_ms[len(call_ms) // 2],
-                   "call_ms_min": call_ms[0], "layers": len(layers),
-                   "tokens_per_s": wl.total_q / (ms_per_step * 1e-3)},
-        "roofline": roof, "cpu_baseline": cpu,
-    }
-    print(json.dumps(line), flush=True)
+    res = {"value": value, "unit": unit, "ms_per_step": ms_per_step, "dtype": dtype, "roofline": roof,
+           "config": {"workload": f"{workload_key(args)} {describe(args)}", "rows": wl.total_q,
+                      "sum_ctx": sum_ctx, "kernel_ms": kernel_ms, "call_ms_median": call_ms[len(call_ms) // 2],
+                      "call_ms_min": call_ms[0], "layers": len(layers),
+                      "tokens_per_s": wl.total_q / (ms_per_step * 1e-3)}}
+    if keep_inputs:
+        res["_inputs"] = (wl, cache, q, ctx)
+    return res
 
 
 if __name__ == "__main__":

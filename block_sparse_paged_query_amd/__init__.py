@@ -13,7 +13,7 @@ Entry points (same names as the C ABI):
 * ``msa_sparse_decode``            - block-sparse GQA decode
 * ``msa_sparse_prefill``           - block-sparse ragged causal prefill
 * ``msa_insert_index_cache``       - index-key side-cache scatter
-* ``msa_debug_dequant_tokens``     - test hook: dequantized K/V of tokens
+* ``msa_debug_gather_dequant``     - test hook: each row's K/V as an attend gathers them
 """
 
 from __future__ import annotations
@@ -28,7 +28,7 @@ __all__ = [
     "MsaError", "KVCache", "library_path", "load_library",
     "msa_build_sparse_block_table", "msa_query_token_positions",
     "msa_sparse_decode", "msa_sparse_prefill", "msa_sparse_attention", "msa_insert_index_cache",
-    "msa_debug_dequant_tokens", "msa_decode_workspace_size",
+    "msa_debug_gather_dequant", "msa_decode_workspace_size",
     "MSA_BF16", "MSA_FP16", "MSA_FP8_E4M3FN", "MSA_NVFP4", "MSA_FP32",
 ]
 
@@ -76,7 +76,7 @@ _SIGS = {
                               _P, _I64, _I32, _P, _I32, _P, _I64, _I32, _P, _P, _F32, _P, _P, _SZ, _P], _I32),
     "msa_insert_index_cache": ([_P, _I64, _I64, _I32, _I32, _I32, _P, _I64, _I64, _I64, _I32, _I32, _P, _I64,
                                 _P], _I32),
-    "msa_debug_dequant_tokens": ([ctypes.POINTER(_KV), _P, _P, _I32, _P, _P, _P], _I32),
+    "msa_debug_gather_dequant": ([ctypes.POINTER(_KV), _P, _I64, _P, _I32, _I32, _I32, _P, _P, _P], _I32),
 }
 _lib = None
 
@@ -414,14 +414,21 @@ def msa_insert_index_cache(index_k, index_cache, index_slot_mapping):
           index_slot_mapping.stride(0), _stream(dev))
 
 
-def msa_debug_dequant_tokens(kv: KVCache, pages, slots):
-    """fp32 K and V ([n, Hkv, D] each) of tokens (page id, slot 0..15), as the kernels decode them."""
+def msa_debug_gather_dequant(kv: KVCache, sparse_bt, sparse_ctx, path="decode"):
+    """fp32 K and V ([rows, 16 * width, Hkv, D] each) of every row's tokens in
+    sparse-table order, as the decode attend's gather (path "decode") or the
+    prefill attend's staging (path "prefill") produces them."""
     dev = kv.k_pages.device
-    _need(pages, "pages", torch.int32, 1, dev)
-    _need(slots, "slots", torch.int32, 1, dev)
-    n = pages.shape[0]
-    k = torch.empty((n, kv.num_kv_heads, kv.head_dim), dtype=torch.float32, device=dev)
+    _need(sparse_bt, "sparse_bt", torch.int32, 2, dev)
+    _need(sparse_ctx, "sparse_ctx", torch.int32, 1, dev)
+    if path not in ("decode", "prefill"):
+        raise ValueError(f"path {path!r}: 'decode' or 'prefill'")
+    rows, width = sparse_bt.shape
+    if sparse_ctx.shape[0] != rows:
+        raise ValueError(f"sparse_ctx has {sparse_ctx.shape[0]} rows, sparse_bt {rows}")
+    k = torch.empty((rows, 16 * width, kv.num_kv_heads, kv.head_dim), dtype=torch.float32, device=dev)
     v = torch.empty_like(k)
     kvs = kv._struct()
-    _call("msa_debug_dequant_tokens", ctypes.byref(kvs), _ptr(pages), _ptr(slots), n, _ptr(k), _ptr(v), _stream(dev))
+    _call("msa_debug_gather_dequant", ctypes.byref(kvs), _ptr(sparse_bt), sparse_bt.stride(0), _ptr(sparse_ctx),
+          rows, width, 0 if path == "decode" else 1, _ptr(k), _ptr(v), _stream(dev))
     return k, v

@@ -339,6 +339,21 @@ __device__ __forceinline__ void v_operands(const ChunkRaw<FMT, D>& raw, u32x4 vo
   }
 }
 
+// NVFP4 V slots are read whole (their tokens are interleaved by 4), so in a
+// context's last chunk the scales of tokens at or past lim are cleared before
+// conversion: their codes are finite, an unwritten scale byte may not be.
+// Lane (r, g) holds the scale bytes of tokens tok0 + 16 t + i (i < 4) of page t.
+template <int D>
+__device__ __forceinline__ void nvfp4_clear_v_scales(ChunkRaw<kFmtNvfp4, D>& rv, int tok0, int lim) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    uint32_t keep = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) keep |= (tok0 + 16 * t + i < lim) ? (0xffu << (8 * i)) : 0u;
+    rv.vs[t] &= keep;
+  }
+}
+
 template <int FMT, int D>
 struct WaveState {
   static constexpr int NN = D / 16;
@@ -411,15 +426,7 @@ __device__ __forceinline__ void compute_chunk(WaveState<FMT, D>& st, const Chunk
   u32x4 vop[NN];
   if constexpr (FMT == kFmtNvfp4) {
     ChunkRaw<FMT, D> rv = raw;
-    if (masked) {   // clear the V scales of tokens at or past lim (page t, byte i: token tok0 + 16t + i)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t keep = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) keep |= (tok0 + 16 * t + i < lim) ? (0xffu << (8 * i)) : 0u;
-        rv.vs[t] &= keep;
-      }
-    }
+    if (masked) nvfp4_clear_v_scales(rv, tok0, lim);
     v_operands<FMT, D>(rv, vop);
   } else {
     v_operands<FMT, D>(raw, vop);
@@ -596,6 +603,105 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const AttendArgs a, i
   uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.out) + ((int64_t)pair * D + d) * 2);
   dst[0] = pack_bf16(o[0] * inv, o[1] * inv);
   dst[1] = pack_bf16(o[2] * inv, o[3] * inv);
+}
+
+// ---------------------------------------------------------------------------
+// Test hook: each row's K and V in sparse-table order, exactly as the decode
+// attend's gather produces its matrix operands.  One wave per (row, kv head)
+// walks the row's 32-token chunks with the attend's own chunk_loc /
+// issue_loads, converts with k_operand / v_operands (and, for NVFP4, the same
+// V-scale clearing in the context's last chunk), and writes each operand
+// element, times k_scale or v_scale in fp32, at its token and d.  Token t of
+// the row is slot t / 128 of sparse_bt (its physical block is the slot's first
+// page id / block_page_stride); tokens at or past ctx are 0.
+// out[row][token][kv head][d], width_tokens tokens per row.
+// ---------------------------------------------------------------------------
+template <int FMT, int D>
+__global__ __launch_bounds__(64) void gather_dequant_decode_kernel(const AttendArgs a, const int32_t* __restrict__ sbt,
+                                                                   int64_t sbt_stride, const int32_t* __restrict__ sctx,
+                                                                   int bps, int width_tokens, float* __restrict__ k_out,
+                                                                   float* __restrict__ v_out) {
+  constexpr int KK = D / 32, NN = D / 16;
+  typedef typename OpType<FMT>::type OT;
+  typedef typename PvType<FMT>::type PT;
+  __shared__ int slot_list[kMaxTopK];
+  const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+  const int kvh = blockIdx.x % a.num_kv_heads;
+  const int64_t row = blockIdx.x / a.num_kv_heads;
+  const int ctx = min(max(sctx[row], 0), width_tokens);
+  const int nslots = (ctx + kBlockTokens - 1) / kBlockTokens;
+  for (int s = lane; s < nslots; s += 64) slot_list[s] = sbt[row * sbt_stride + kPagesPerBlock * s] / bps;
+  __syncthreads();
+  const int nchunks = (ctx + 31) >> 5;
+  const LaneOffsets lo = lane_offsets<FMT, D>(lane, a.row_stride);
+  const float ks = a.k_scale ? *a.k_scale : 1.f, vs = a.v_scale ? *a.v_scale : 1.f;
+  const int64_t tok_stride = (int64_t)a.num_kv_heads * D;
+  float* kb = k_out + (row * width_tokens * a.num_kv_heads + kvh) * D;
+  float* vb = v_out + (row * width_tokens * a.num_kv_heads + kvh) * D;
+  for (int c = 0; c < nchunks; ++c) {
+    ChunkRaw<FMT, D> raw;
+    const ChunkLoc L = chunk_loc<FMT, D>(a, slot_list, c, nchunks, ctx, kvh);
+    issue_loads<FMT, D, 0>(raw, L, lo);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const OT op = k_operand<FMT, D>(raw, t, kk);
+        float* dst = kb + (int64_t)(c * 32 + 16 * t + r) * tok_stride + kappa<FMT, D>(kk, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = (float)op[e] * ks;
+      }
+    }
+    const bool masked = !L.ok || c * 32 + 32 > ctx;
+    u32x4 vop[NN];
+    if constexpr (FMT == kFmtNvfp4) {
+      ChunkRaw<FMT, D> rv = raw;
+      if (masked) nvfp4_clear_v_scales(rv, c * 32 + 4 * g, L.ok ? ctx : 0);
+      v_operands<FMT, D>(rv, vop);
+    } else {
+      v_operands<FMT, D>(raw, vop);
+    }
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) {
+      const PT op = __builtin_bit_cast(PT, vop[nn]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {   // row i of the operand: chunk token tau(8g + i)
+        const int tok = c * 32 + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
+        vb[(int64_t)tok * tok_stride + r * NN + nn] = (float)op[i] * vs;
+      }
+    }
+  }
+  // slots past the context
+  for (int idx = nchunks * 32 * D + lane; idx < width_tokens * D; idx += 64) {
+    const int64_t off = (int64_t)(idx / D) * tok_stride + idx % D;
+    kb[off] = 0.f;
+    vb[off] = 0.f;
+  }
+}
+
+hipError_t launch_gather_dequant_decode(const AttendArgs& a, int fmt, const int32_t* sbt, int64_t sbt_stride,
+                                        const int32_t* sctx, int bps, int rows, int width_tokens, float* k_out,
+                                        float* v_out, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)rows * a.num_kv_heads)), block(64);
+  if (a.head_dim == 128) {
+    if (fmt == kFmtBf16)
+      hipLaunchKernelGGL((gather_dequant_decode_kernel<kFmtBf16, 128>), grid, block, 0, stream, a, sbt, sbt_stride,
+                         sctx, bps, width_tokens, k_out, v_out);
+    else if (fmt == kFmtFp8)
+      hipLaunchKernelGGL((gather_dequant_decode_kernel<kFmtFp8, 128>), grid, block, 0, stream, a, sbt, sbt_stride,
+                         sctx, bps, width_tokens, k_out, v_out);
+    else
+      hipLaunchKernelGGL((gather_dequant_decode_kernel<kFmtNvfp4, 128>), grid, block, 0, stream, a, sbt, sbt_stride,
+                         sctx, bps, width_tokens, k_out, v_out);
+  } else {
+    if (fmt == kFmtBf16)
+      hipLaunchKernelGGL((gather_dequant_decode_kernel<kFmtBf16, 64>), grid, block, 0, stream, a, sbt, sbt_stride,
+                         sctx, bps, width_tokens, k_out, v_out);
+    else
+      hipLaunchKernelGGL((gather_dequant_decode_kernel<kFmtFp8, 64>), grid, block, 0, stream, a, sbt, sbt_stride,
+                         sctx, bps, width_tokens, k_out, v_out);
+  }
+  return hipGetLastError();
 }
 
 // Waves per workgroup: 4 unless fewer waves fill the machine in fewer,

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <string.h>
 
+
 #include "../../include/msa.h"
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -471,28 +472,35 @@ MSA_API msa_status_t msa_insert_index_cache(const void* index_k, int64_t k_strid
                     "index cache launch");
 }
 
-MSA_API msa_status_t msa_debug_dequant_tokens(const msa_kv_cache_t* kv, const int32_t* pages, const int32_t* slots,
-                                              int32_t n, float* k_out, float* v_out, hipStream_t stream) {
-  MSA_CHECK(kv != nullptr && n >= 0, MSA_ERR_INVALID_ARGUMENT, "NULL kv or negative n");
-  MSA_CHECK(fmt_of(kv->kv_dtype) >= 0, MSA_ERR_UNSUPPORTED, "kv dtype %d", kv->kv_dtype);
-  MSA_CHECK(kv->head_dim >= 16 && kv->head_dim % 16 == 0 && kv->num_kv_heads >= 1, MSA_ERR_INVALID_ARGUMENT,
-            "head_dim %d / num_kv_heads %d", kv->head_dim, kv->num_kv_heads);
-  MSA_CHECK(kv->kv_dtype != MSA_NVFP4 || kv->head_dim == 128, MSA_ERR_UNSUPPORTED,
-            "nvfp4 pages need head_dim 128 (got %d)", kv->head_dim);
+MSA_API msa_status_t msa_debug_gather_dequant(const msa_kv_cache_t* kv, const int32_t* sparse_bt,
+                                              int64_t sbt_row_stride, const int32_t* sparse_ctx, int32_t total_q,
+                                              int32_t sbt_width, int32_t path, float* k_out, float* v_out,
+                                              hipStream_t stream) {
+  MSA_CHECK(kv != nullptr && total_q >= 0, MSA_ERR_INVALID_ARGUMENT, "NULL kv or negative total_q");
+  MSA_CHECK(fmt_of(kv->kv_dtype) >= 0, MSA_ERR_UNSUPPORTED, "kv dtype %d: bf16, fp8 e4m3fn or nvfp4 pages only",
+            kv->kv_dtype);
+  MSA_CHECK(kv->num_kv_heads >= 1, MSA_ERR_INVALID_ARGUMENT, "num_kv_heads %d < 1", kv->num_kv_heads);
+  MSA_CHECK(path == 0 || path == 1, MSA_ERR_INVALID_ARGUMENT, "path %d: 0 (decode gather) or 1 (prefill staging)",
+            path);
+  MSA_CHECK(kv->head_dim == 128 || (kv->head_dim == 64 && path == 0 && kv->kv_dtype != MSA_NVFP4),
+            MSA_ERR_UNSUPPORTED, "head_dim %d: 128, or 64 for bf16 / fp8 pages on the decode path", kv->head_dim);
   {
     const msa_status_t st = check_kv_geometry(kv);
     if (st != MSA_OK) return st;
   }
-  if (n == 0) return ok();
+  MSA_CHECK(sbt_width >= msa::kPagesPerBlock && sbt_width % msa::kPagesPerBlock == 0 &&
+                sbt_width <= msa::kPagesPerBlock * msa::kMaxTopK,
+            MSA_ERR_INVALID_ARGUMENT, "sbt_width %d: a multiple of 8 in 8..%d", sbt_width,
+            msa::kPagesPerBlock * msa::kMaxTopK);
+  MSA_CHECK(sbt_row_stride >= sbt_width, MSA_ERR_INVALID_ARGUMENT, "sparse_bt row stride %lld < sbt_width %d",
+            (long long)sbt_row_stride, sbt_width);
+  if (total_q == 0) return ok();
   const bool v_plane = kv->kv_dtype != MSA_NVFP4 && kv->kv_layout == MSA_KV_PAGE16;
-  MSA_CHECK(pages && slots && k_out && v_out && kv->k_pages && (!v_plane || kv->v_pages),
+  MSA_CHECK(sparse_bt && sparse_ctx && k_out && v_out && kv->k_pages && (!v_plane || kv->v_pages),
             MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  msa::DequantArgs a;
+  msa::AttendArgs a;
+  memset(&a, 0, sizeof(a));
   const KvGeometry g = kv_geometry(kv);
-  a.fmt = fmt_of(kv->kv_dtype);
-  a.num_kv_heads = kv->num_kv_heads;
-  a.head_dim = kv->head_dim;
-  a.block_page_stride = kv->block_page_stride;
   a.k_base = g.k_base;
   a.v_base = g.v_base;
   a.blk_units = g.blk_units;
@@ -503,12 +511,16 @@ MSA_API msa_status_t msa_debug_dequant_tokens(const msa_kv_cache_t* kv, const in
   a.v_unit_offset = g.v_unit_offset;
   a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale;
-  a.pages = pages;
-  a.slots = slots;
-  a.n = n;
-  a.k_out = k_out;
-  a.v_out = v_out;
-  return hip_status(msa::launch_debug_dequant(a, stream), "dequant hook launch");
+  a.num_kv_heads = kv->num_kv_heads;
+  a.head_dim = kv->head_dim;
+  const int width_tokens = sbt_width * msa::kPageTokens;
+  const int fmt = fmt_of(kv->kv_dtype);
+  const hipError_t e = path == 0
+      ? msa::launch_gather_dequant_decode(a, fmt, sparse_bt, sbt_row_stride, sparse_ctx, kv->block_page_stride,
+                                          total_q, width_tokens, k_out, v_out, stream)
+      : msa::launch_gather_dequant_prefill(a, fmt, sparse_bt, sbt_row_stride, sparse_ctx, kv->block_page_stride,
+                                           total_q, width_tokens, k_out, v_out, stream);
+  return hip_status(e, "gather dequant hook launch");
 }
 
 }  // extern "C"

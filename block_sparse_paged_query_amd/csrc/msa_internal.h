@@ -88,28 +88,15 @@ hipError_t launch_index_insert(const void* k, int64_t ks0, int64_t ks1, int n, i
                                int64_t cs0, int64_t cs1, int num_blocks, int block_size, const int64_t* slots,
                                int64_t slot_stride, hipStream_t stream);
 
-struct DequantArgs {
-  int fmt;
-  int num_kv_heads;
-  int head_dim;
-  int block_page_stride;    // page-16 id p names page p % block_page_stride of block p / block_page_stride
-  const uint8_t* k_base;   // geometry as in AttendArgs
-  const uint8_t* v_base;
-  int32_t blk_units;
-  int32_t head_stride;
-  int64_t sub_stride;
-  int32_t row_stride;
-  int64_t num_units;
-  int32_t v_unit_offset;
-  const float* k_scale;
-  const float* v_scale;
-  const int32_t* pages;
-  const int32_t* slots;
-  int n;
-  float* k_out;
-  float* v_out;
-};
+// Test hook: each row's K / V in sparse-table order through the decode
+// attend's gather (launch_gather_dequant_decode) or the prefill attend's
+// staged copy (launch_gather_dequant_prefill; head_dim 128).
+hipError_t launch_gather_dequant_decode(const AttendArgs& a, int fmt, const int32_t* sbt, int64_t sbt_stride,
+                                        const int32_t* sctx, int bps, int rows, int width_tokens, float* k_out,
+                                        float* v_out, hipStream_t stream);
+hipError_t launch_gather_dequant_prefill(const AttendArgs& a, int fmt, const int32_t* sbt, int64_t sbt_stride,
+                                         const int32_t* sctx, int bps, int rows, int width_tokens, float* k_out,
+                                         float* v_out, hipStream_t stream);
 
-hipError_t launch_debug_dequant(const DequantArgs& a, hipStream_t stream);
 
 }  // namespace msa

@@ -696,6 +696,108 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   }
 }
 
+// ---------------------------------------------------------------------------
+// Test hook: each row's K and V in sparse-table order, exactly as the prefill
+// attend stages them.  One workgroup per (row, kv head, slot): the slot's
+// block goes into LDS through the attend's own copy (pf_issue_block for bf16
+// pages, pf_stage_issue for fp8 / NVFP4), and each (key, 16-element piece) is
+// read back in the compute types: bf16 keys and values as copied, staged
+// formats through pf_stage_item.  Values are the operand elements times
+// k_scale / v_scale in fp32; keys at or past the row's context in the slot,
+// and blocks outside the cache, give 0.  out[row][token][kv head][d].
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ __launch_bounds__(kPfThreads) void gather_dequant_prefill_kernel(const AttendArgs a,
+                                                                            const int32_t* __restrict__ sbt,
+                                                                            int64_t sbt_stride,
+                                                                            const int32_t* __restrict__ sctx, int bps,
+                                                                            int width_tokens, float* __restrict__ k_out,
+                                                                            float* __restrict__ v_out) {
+  constexpr int D = 128;
+  __shared__ __align__(16) uint8_t bK[FMT == kFmtBf16 ? kPfBlockBytes : 16];
+  __shared__ __align__(16) uint8_t bV[FMT == kFmtBf16 ? kPfBlockBytes : kPfRawBytes<FMT>];
+  const int tid = threadIdx.x;
+  const int nslot = width_tokens / kBlockTokens;
+  const int slot = blockIdx.x % nslot;
+  const int kvh = (blockIdx.x / nslot) % a.num_kv_heads;
+  const int64_t row = blockIdx.x / nslot / a.num_kv_heads;
+  const int ctx = min(max(sctx[row], 0), width_tokens);
+  const int nkeys = min(ctx - slot * kBlockTokens, kBlockTokens);   // <= 0: slot past the context
+  int phys = nkeys > 0 ? sbt[row * sbt_stride + kPagesPerBlock * slot] / bps : -1;
+  const bool inside = phys >= 0 && (int64_t)phys * a.blk_units + a.v_unit_offset + kPagesPerBlock - 1 < a.num_units;
+  const float ks = a.k_scale ? *a.k_scale : 1.f, vs = a.v_scale ? *a.v_scale : 1.f;
+  const int64_t tok_stride = (int64_t)a.num_kv_heads * D;
+  float* kb = k_out + ((row * width_tokens + slot * kBlockTokens) * a.num_kv_heads + kvh) * D;
+  float* vb = v_out + ((row * width_tokens + slot * kBlockTokens) * a.num_kv_heads + kvh) * D;
+  if (inside) {   // uniform
+    if constexpr (FMT == kFmtBf16) {
+      pf_issue_block((lds_u8*)bK, (lds_u8*)bV, a, kvh, phys, 0, nkeys);
+    } else {
+      pf_stage_issue<FMT>((lds_u8*)bV, a, kvh, phys);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  // item q: side q / 1024, key, 16-element piece n (d = 16 n .. 16 n + 15)
+  for (int q = tid; q < 2 * kBlockTokens * 8; q += kPfThreads) {
+    const bool v_side = q >= kBlockTokens * 8;
+    const int key = (q >> 3) & (kBlockTokens - 1), n = q & 7;
+    uint32_t o[8];
+    if constexpr (FMT == kFmtBf16) {
+      // K rows: 16-byte chunk c of key at chunk c ^ (key & 15); V: chunk lc of
+      // key in the 16-byte slot ((lc / 2) * 128 + key) * 2 + lc % 2
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * n + h;
+        const uint8_t* src = v_side ? bV + (((c >> 1) * kBlockTokens + key) * 2 + (c & 1)) * 16
+                                    : bK + key * 256 + ((c ^ k_swz(key)) << 4);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+        o[4 * h + 0] = w[0];
+        o[4 * h + 1] = w[1];
+        o[4 * h + 2] = w[2];
+        o[4 * h + 3] = w[3];
+      }
+    } else {
+      pf_stage_item<FMT>(bV, v_side, key, n, o);
+    }
+    const bool keep = inside && key < nkeys;
+    float* dst = (v_side ? vb : kb) + (int64_t)key * tok_stride + 16 * n;
+    const float sc = v_side ? vs : ks;
+    // element types: bf16 pages bf16; fp8 K bf16, V fp16; NVFP4 fp16
+    const bool as_f16 = FMT == kFmtNvfp4 || (FMT == kFmtFp8 && v_side);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float lo, hi;
+      if (as_f16) {
+        const f16x2 p = bits_f16x2(o[i]);
+        lo = (float)p[0];
+        hi = (float)p[1];
+      } else {
+        lo = __uint_as_float(o[i] << 16);
+        hi = __uint_as_float(o[i] & 0xffff0000u);
+      }
+      dst[2 * i] = keep ? lo * sc : 0.f;
+      dst[2 * i + 1] = keep ? hi * sc : 0.f;
+    }
+  }
+}
+
+hipError_t launch_gather_dequant_prefill(const AttendArgs& a, int fmt, const int32_t* sbt, int64_t sbt_stride,
+                                         const int32_t* sctx, int bps, int rows, int width_tokens, float* k_out,
+                                         float* v_out, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)rows * a.num_kv_heads * (width_tokens / kBlockTokens))), block(kPfThreads);
+  if (fmt == kFmtBf16)
+    hipLaunchKernelGGL(gather_dequant_prefill_kernel<kFmtBf16>, grid, block, 0, stream, a, sbt, sbt_stride, sctx, bps,
+                       width_tokens, k_out, v_out);
+  else if (fmt == kFmtFp8)
+    hipLaunchKernelGGL(gather_dequant_prefill_kernel<kFmtFp8>, grid, block, 0, stream, a, sbt, sbt_stride, sctx, bps,
+                       width_tokens, k_out, v_out);
+  else
+    hipLaunchKernelGGL(gather_dequant_prefill_kernel<kFmtNvfp4>, grid, block, 0, stream, a, sbt, sbt_stride, sctx,
+                       bps, width_tokens, k_out, v_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t stream) {
   const int QT = kPfWaves * kPfTiles * (16 / a.group);
   // tiles: ceil(rows / QT) per request and per padding range (before the

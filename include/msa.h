@@ -293,16 +293,30 @@ MSA_API msa_status_t msa_insert_index_cache(
     const int64_t* slot_mapping, int64_t slot_stride, hipStream_t stream);
 
 /*
- * Test hook: the dequantized K and V of n tokens, through the same device
- * conversions the attends use.  pages [n], slots [n] int32 (page id and
- * token 0..15 within it); k_out, v_out [n][num_kv_heads][head_dim] fp32 =
- * stored value (bf16 / fp8 / e2m1 x block scale) x k_scale or v_scale,
- * rounded to nearest fp32.  V is read at page + (block_page_stride - 8)
- * for bf16 / fp8.  Tokens whose page is outside [0, num_pages) give NaN.
+ * Test hook: every row's K and V in sparse-table order, as an attend's own
+ * gather and dequant produce its matrix operands.  [NV4] customize_spec (the
+ * two NVFP4 head slots, codes plus block scales) and [FI]
+ * MiniMaxM3SparseFlashInferImpl.forward (the fp8 view and its per-tensor
+ * scales); the table is msa_build_sparse_block_table's
+ * ([SPA] _write_sparse_block_table_row_from_values).
+ *
+ * sparse_bt [total_q][sbt_width] int32 (row stride sbt_row_stride), page-16
+ * ids; sparse_ctx [total_q] int32.  Token t < sparse_ctx[i] of row i lies in
+ * slot t / 128, whose physical block is sparse_bt[i][8 * (t / 128)] /
+ * block_page_stride, at offset t % 128 of the block.
+ * path 0: the decode attend's gather (chunk addressing, page loads masked at
+ *   the context, in-register conversion to the operand types);
+ * path 1: the prefill attend's staging (the block copied into LDS, fp8 /
+ *   NVFP4 converted there; head_dim 128).
+ * k_out, v_out [total_q][16 * sbt_width][num_kv_heads][head_dim] fp32: the
+ * operand element (bf16 / fp8 / e2m1 x E4M3 block scale, exact in the
+ * operand type) times k_scale or v_scale, rounded to nearest fp32.  Tokens at
+ * or past sparse_ctx[i], and blocks outside [0, num_pages), give 0.
+ * sbt_width: a multiple of 8, at most 8 * 1024.
  */
-MSA_API msa_status_t msa_debug_dequant_tokens(
-    const msa_kv_cache_t* kv, const int32_t* pages, const int32_t* slots, int32_t n,
-    float* k_out, float* v_out, hipStream_t stream);
+MSA_API msa_status_t msa_debug_gather_dequant(
+    const msa_kv_cache_t* kv, const int32_t* sparse_bt, int64_t sbt_row_stride, const int32_t* sparse_ctx,
+    int32_t total_q, int32_t sbt_width, int32_t path, float* k_out, float* v_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

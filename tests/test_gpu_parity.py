@@ -18,6 +18,7 @@ import oracle
 import block_sparse_paged_query_amd as msa
 from synth import make_workload, make_kv_cache, make_query, rows128_cache, written_blocks
 from tests.helpers import attention_within_tolerance, compact_oracle_inputs, oracle_cache, oracle_positions, q_f64
+from tests.oracle_pool import sparse_attention_rows
 
 pytestmark = pytest.mark.gpu
 ATOL = 1e-2
@@ -92,55 +93,88 @@ def test_table_edge_rows():
 
 # ---------------------------------------------------------------- dequant
 
-def _hook_vs_oracle(wl, cache, pages, slots):
+def _hook_vs_oracle(wl, cache, rows=None, paths=("decode", "prefill"), table=None):
+    """The gather-order hook (each attend's own gather and dequant) against the
+    oracle: row i's token t < ctx is read by plain indexing at page
+    sbt[i][t // 16], slot t % 16, and its fp64 value x scale rounded to fp32;
+    tokens past ctx are 0.  Bit-exact, NaN where the oracle gives NaN."""
     kv = _kv(wl, cache)
-    k, v = msa.msa_debug_dequant_tokens(kv, _dev(pages), _dev(slots))
+    if table is None:
+        req, pos = oracle_positions(wl)
+        rows = np.arange(wl.total_q) if rows is None else np.asarray(rows)
+        sbt, ctx = oracle.sparse_block_table(wl.topk[rows], wl.block_table, req[rows], pos[rows],
+                                             wl.block_page_stride)
+    else:
+        sbt, ctx = table
     oc = oracle_cache(wl, cache)
-    wk = oc.read_tokens("k", pages, slots).astype(np.float32)
-    wv = oc.read_tokens("v", pages, slots).astype(np.float32)
-    for got, want in ((k.cpu().numpy(), wk), (v.cpu().numpy(), wv)):
-        nan = np.isnan(want)
-        assert (np.isnan(got) == nan).all()
-        assert (got[~nan].view(np.uint32) == want[~nan].view(np.uint32)).all()
+    n, width = sbt.shape
+    want_k = np.zeros((n, 16 * width, wl.num_kv_heads, wl.head_dim), np.float32)
+    want_v = np.zeros_like(want_k)
+    for i in range(n):
+        t = np.arange(int(ctx[i]))
+        pages, slots = sbt[i][t // 16], t % 16
+        want_k[i, :len(t)] = oc.read_tokens("k", pages, slots).astype(np.float32)
+        want_v[i, :len(t)] = oc.read_tokens("v", pages, slots).astype(np.float32)
+    for path in paths:
+        k, v = msa.msa_debug_gather_dequant(kv, _dev(sbt), _dev(ctx), path=path)
+        for side, got, want in (("k", k.cpu().numpy(), want_k), ("v", v.cpu().numpy(), want_v)):
+            nan = np.isnan(want)
+            assert (np.isnan(got) == nan).all(), f"{path} {side}: NaN positions differ"
+            bad = got[~nan].view(np.uint32) != want[~nan].view(np.uint32)
+            assert not bad.any(), f"{path} {side}: {int(bad.sum())} elements differ"
+    return int(np.sum(ctx))
 
 
-@pytest.mark.parametrize("name,layout", [("C3s", "page16"), ("C5s", "page16"), ("C2s", "page16"),
-                                         ("C2s", "rows128"), ("C3s", "rows128")])
-def test_dequant_hook_bit_exact_on_written_tokens(name, layout):
+@pytest.mark.parametrize("name,layout", [("C2s", "page16"), ("C3s", "page16"), ("C5s", "page16"),
+                                         ("C4s", "page16"), ("C2s", "rows128"), ("C3s", "rows128")])
+def test_gather_dequant_bit_exact(name, layout):
+    # every row's tokens in sparse-table order, through the decode gather and
+    # the prefill staging, on the reduced workloads
     wl = make_workload(name)
     cache = make_kv_cache(wl, DEV)
     if layout == "rows128":
         cache = rows128_cache(cache, wl, layers=2, layer=1)
-    pages, slots = [], []
-    for (r, b, n) in written_blocks(wl):
-        phys = int(wl.block_table[r, b])
-        for t in range(n):
-            pages.append(phys * wl.block_page_stride + t // 16)
-            slots.append(t % 16)
-    _hook_vs_oracle(wl, cache, np.array(pages), np.array(slots))
+    assert _hook_vs_oracle(wl, cache, rows=C4S_ROWS if name == "C4s" else None) > 0
 
 
-def test_dequant_hook_exhaustive_codes():
-    # fp8: all 256 codes; NVFP4: all 16 x 256 (code, scale) pairs, NaN scales included
+# C4s rows (requests of 300 and 517 new tokens, 5 padded rows): request and
+# block edges, and padding
+C4S_ROWS = [0, 1, 127, 128, 299, 300, 301, 555, 700, 816, 817, 818, 821]
+
+
+@pytest.mark.parametrize("name,kw", [("C4s", dict(kv_dtype="fp8")), ("C4s", dict(kv_dtype="nvfp4")),
+                                     ("C3s", dict(block_page_stride=16))])
+def test_gather_dequant_bit_exact_variants(name, kw):
+    wl = make_workload(name, **kw)
+    _hook_vs_oracle(wl, make_kv_cache(wl, DEV), rows=C4S_ROWS if name == "C4s" else None)
+
+
+def test_gather_dequant_full_size_c5_sampled():
+    # NVFP4 decode at its full size: 8 rows' 4096-token contexts
+    wl = make_workload("C5")
+    _hook_vs_oracle(wl, make_kv_cache(wl, DEV), rows=[0, 1, 31, 64, 65, 100, 126, 127])
+
+
+def test_gather_dequant_exhaustive_codes():
+    # fp8: all 256 codes in one block; NVFP4: all 16 x 256 (code, scale) pairs,
+    # NaN scales included, in the K and the V slot of one block
+    table = (np.array([np.arange(8)]), np.array([128]))
     wl = make_workload("C1", kv_dtype="fp8", Hq=1, Hkv=1, D=128)
-    codes = torch.arange(256, dtype=torch.uint8, device=DEV).repeat(8).view(1, 1, 16, 128)
-    cache = dict(k_pages=codes.clone(), v_pages=codes.flip(-1).contiguous(), k_scale=0.75, v_scale=1.0 / 3.0,
-                 page_stride_bytes=2048, num_pages=1)
-    cache["v_scale"] = float(np.float32(cache["v_scale"]))
-    _hook_vs_oracle(wl, cache, np.zeros(16, dtype=np.int64), np.arange(16))
+    codes = torch.arange(256, dtype=torch.uint8, device=DEV).repeat(64).view(8, 1, 16, 128)
+    cache = dict(k_pages=codes.clone(), v_pages=codes.flip(-1).contiguous(), k_scale=float(np.float32(0.75)),
+                 v_scale=float(np.float32(1.0 / 3.0)))
+    _hook_vs_oracle(wl, cache, table=table)
     wl4 = make_workload("C1", kv_dtype="nvfp4", Hq=1, Hkv=1, D=128)
-    pages = torch.zeros((2, 2, 9 * 128), dtype=torch.uint8)
+    pages = torch.zeros((8, 2, 9 * 128), dtype=torch.uint8)
     nib = torch.arange(16, dtype=torch.uint8)
-    for p in range(2):
-        for s in range(2):
-            data = (nib.repeat(16 * 8)[0::2] | (nib.repeat(16 * 8)[1::2] << 4)).view(16, 64)
-            pages[p, s, :1024] = torch.roll(data.reshape(-1), shifts=s)
-            pages[p, s, 1024:] = torch.arange(128, dtype=torch.uint8) + 128 * p
+    data = (nib.repeat(16 * 8)[0::2] | (nib.repeat(16 * 8)[1::2] << 4)).view(16, 64)   # element d holds code d % 16
+    for p in range(8):
+        for side in range(2):
+            pages[p, side, :1024] = torch.roll(data.reshape(-1), shifts=side + p)
+            pages[p, side, 1024:] = torch.arange(128, dtype=torch.uint8) + 128 * (p % 2)
     cache4 = dict(k_pages=pages.to(DEV), v_pages=None, k_scale=float(np.float32(0.0123)),
-                  v_scale=float(np.float32(3.5)), page_stride_bytes=2 * 9 * 128, num_pages=2)
-    pg = np.repeat(np.arange(2), 16)
-    sl = np.tile(np.arange(16), 2)
-    _hook_vs_oracle(wl4, cache4, pg, sl)
+                  v_scale=float(np.float32(3.5)))
+    _hook_vs_oracle(wl4, cache4, table=table)
 
 
 # ---------------------------------------------------------------- attention
@@ -152,12 +186,13 @@ def _parity(wl, rows=None, cache=None):
     req, pos = oracle_positions(wl)
     rows = np.arange(wl.total_q) if rows is None else np.asarray(rows)
     oc, bt, _, _ = compact_oracle_inputs(wl, cache, rows)
-    qf = np.zeros((wl.total_q, wl.num_q_heads, wl.head_dim))   # only sampled rows are read
-    qf[rows] = q_f64(q[torch.from_numpy(rows).to(DEV)])
-    want = oracle.sparse_attention(qf, oc, wl.topk, bt, req, pos, wl.softmax_scale, rows=rows)
+    qr = q_f64(q[torch.from_numpy(rows).to(DEV)])
+    want = sparse_attention_rows(oc, bt, qr, wl.topk[rows], req[rows], pos[rows], wl.softmax_scale)
     got = out.float().cpu().numpy()[rows]
     assert np.isfinite(got).all()
     ok, err, n_big, big_ratio = attention_within_tolerance(got, want, ATOL)
+    print(f"[parity] {wl.name} {wl.kv_dtype}: {len(rows)} rows, max abs error {err:.3e} where |oracle| < 4; "
+          f"{n_big} elements with |oracle| >= 4 at {big_ratio:.3f} of their bound", flush=True)
     assert ok, (f"max abs error {err} (|want| < 4); {n_big} elements with |want| >= 4 held to 1e-2 + half a bf16 "
                 f"spacing, worst at {big_ratio:.3f} of that bound")
     return out, err
@@ -208,21 +243,35 @@ def test_prefill_parity_variants(kw):
     _parity(make_workload("C4s", **kw))
 
 
-@pytest.mark.parametrize("name,rows", [
-    ("C2", [0, 17, 33, 63]),
-    ("C3", [0, 1, 2, 3, 70, 127]),
-    ("C5", [0, 64, 127]),
-])
-def test_decode_parity_full_size_sampled(name, rows):
-    _parity(make_workload(name), rows)
+@pytest.mark.parametrize("name", ["C2", "C3", "C5"])
+def test_decode_parity_full_size_every_row(name):
+    # every row of the named decode workloads at their full sizes
+    _parity(make_workload(name))
 
 
-@pytest.mark.parametrize("kv_dtype,selection", [("bf16", "independent"), ("fp8", "independent"),
-                                                ("nvfp4", "independent"), ("bf16", "per_block")])
-def test_prefill_parity_full_size_sampled(kv_dtype, selection):
+def _c4_stratified_rows(wl, seed=7, n_random=1024):
+    """Every row of the first request and every padded row; for the other
+    requests the first and last row of every 32-row query tile (so of every
+    128-row block too); plus random rows."""
+    cu = wl.cu_seqlens_q
+    rows = set(range(int(cu[0]), int(cu[1]))) | set(range(int(cu[-1]), wl.total_q))
+    for r in range(1, len(cu) - 1):
+        for t0 in range(int(cu[r]), int(cu[r + 1]), 32):
+            rows.update((t0, min(t0 + 31, int(cu[r + 1]) - 1)))
+    rng = np.random.default_rng(seed)
+    rows.update(rng.choice(int(cu[-1]), size=n_random, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("kv_dtype,selection,every_row", [("bf16", "independent", True),
+                                                          ("fp8", "independent", False),
+                                                          ("nvfp4", "independent", False),
+                                                          ("bf16", "per_block", False)])
+def test_prefill_parity_full_size(kv_dtype, selection, every_row):
+    # C4 at its full size: every row on bf16 pages, a stratified ~4400-row set
+    # for the fp8 / NVFP4 pages and the per-block-selection variant
     wl = make_workload("C4", kv_dtype=kv_dtype, selection=selection)
-    rows = [0, 127, 128, 2047, 2048, 6000, 14335, 14336, 22527, 22528, 22591]
-    _parity(wl, rows)
+    _parity(wl, None if every_row else _c4_stratified_rows(wl))
 
 
 @pytest.mark.parametrize("name,cols", [("C4s", 2050), ("C4s:fp8", 2050), ("C2s", 4100)])
@@ -514,18 +563,23 @@ def test_blocks_outside_the_cache_are_skipped(name):
 
 # ---------------------------------------------------------------- index cache
 
-def test_index_cache_insert_bit_exact():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32, torch.float8_e4m3fn])
+def test_index_cache_insert_bit_exact(dtype):
+    # 1-, 2- and 4-byte keys; key rows 2 D apart (a view); padding slots (-1) skipped
     g = torch.Generator().manual_seed(5)
     N, B, T, D = 300, 12, 64, 128
-    k = torch.randn(N, D, generator=g).to(torch.bfloat16)
-    cache = torch.randn(B, T, D, generator=g).to(torch.bfloat16)
+    k_full = torch.randn(N, 2 * D, generator=g).to(dtype)
+    k = k_full[:, :D]
+    cache = torch.randn(B, T, D, generator=g).to(dtype)
     slots = torch.randperm(B * T, generator=g)[:N].to(torch.int64)
     slots[::7] = -1
-    want = oracle.insert_index_cache(k.float().numpy(), cache.float().numpy().copy(), slots.numpy())
+    raw = lambda t: t.contiguous().view(torch.uint8 if t.element_size() == 1 else
+                                        (torch.int16 if t.element_size() == 2 else torch.int32)).numpy()
+    want = oracle.insert_index_cache(raw(k), raw(cache).copy(), slots.numpy())
     gc = cache.to(DEV)
-    msa.msa_insert_index_cache(k.to(DEV), gc, slots.to(DEV))
+    msa.msa_insert_index_cache(k_full.to(DEV)[:, :D], gc, slots.to(DEV))
     torch.cuda.synchronize()
-    assert (gc.float().cpu().numpy() == want).all()
+    assert (raw(gc.cpu()) == want).all()
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(Hq=16, Hkv=4), dict(kv_dtype="fp8")])
