@@ -311,7 +311,9 @@ MSA_API msa_status_t msa_insert_index_cache(
  * k_out, v_out [total_q][16 * sbt_width][num_kv_heads][head_dim] fp32: the
  * operand element (bf16 / fp8 / e2m1 x E4M3 block scale, exact in the
  * operand type) times k_scale or v_scale, rounded to nearest fp32.  Tokens at
- * or past sparse_ctx[i], and blocks outside [0, num_pages), give 0.
+ * or past sparse_ctx[i], and blocks outside [0, num_pages), give zero (an
+ * NVFP4 V element past the context may be -0: its scale is cleared, its
+ * unwritten code keeps its sign).
  * sbt_width: a multiple of 8, at most 8 * 1024.
  */
 MSA_API msa_status_t msa_debug_gather_dequant(

@@ -115,13 +115,18 @@ def _hook_vs_oracle(wl, cache, rows=None, paths=("decode", "prefill"), table=Non
         pages, slots = sbt[i][t // 16], t % 16
         want_k[i, :len(t)] = oc.read_tokens("k", pages, slots).astype(np.float32)
         want_v[i, :len(t)] = oc.read_tokens("v", pages, slots).astype(np.float32)
+    inside = np.arange(16 * width)[None, :] < np.asarray(ctx)[:, None]      # [rows, tokens]
     for path in paths:
         k, v = msa.msa_debug_gather_dequant(kv, _dev(sbt), _dev(ctx), path=path)
         for side, got, want in (("k", k.cpu().numpy(), want_k), ("v", v.cpu().numpy(), want_v)):
-            nan = np.isnan(want)
-            assert (np.isnan(got) == nan).all(), f"{path} {side}: NaN positions differ"
-            bad = got[~nan].view(np.uint32) != want[~nan].view(np.uint32)
+            g_in, w_in = got[inside], want[inside]
+            nan = np.isnan(w_in)
+            assert (np.isnan(g_in) == nan).all(), f"{path} {side}: NaN positions differ"
+            bad = g_in[~nan].view(np.uint32) != w_in[~nan].view(np.uint32)
             assert not bad.any(), f"{path} {side}: {int(bad.sum())} elements differ"
+            # past the context: zero (an NVFP4 V slot's cleared scale times an
+            # unwritten negative code gives -0)
+            assert (got[~inside] == 0).all(), f"{path} {side}: nonzero past the context"
     return int(np.sum(ctx))
 
 
