@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
 * ``msa_build_sparse_block_table`` - page-16 sparse table + context lengths
 * ``msa_query_token_positions``    - prefill request ids and positions
 * ``msa_sparse_decode``            - block-sparse GQA decode
+* ``msa_sparse_decode_noalloc``    - the same decode with no workspace (library-held scratch)
 * ``msa_sparse_prefill``           - block-sparse ragged causal prefill
 * ``msa_insert_index_cache``       - index-key side-cache scatter
 * ``msa_debug_gather_dequant``     - test hook: each row's K/V as an attend gathers them
@@ -27,7 +28,7 @@ import torch
 __all__ = [
     "MsaError", "KVCache", "library_path", "load_library",
     "msa_build_sparse_block_table", "msa_query_token_positions",
-    "msa_sparse_decode", "msa_sparse_prefill", "msa_sparse_attention", "msa_insert_index_cache",
+    "msa_sparse_decode", "msa_sparse_decode_noalloc", "msa_sparse_prefill", "msa_sparse_attention", "msa_insert_index_cache",
     "msa_debug_gather_dequant", "msa_decode_workspace_size",
     "MSA_BF16", "MSA_FP16", "MSA_FP8_E4M3FN", "MSA_NVFP4", "MSA_FP32",
 ]
@@ -69,6 +70,9 @@ _SIGS = {
     "msa_decode_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_decode": ([_P, _I32, _I32, _I32, _I32, ctypes.POINTER(_KV), _P, _I64, _I32, _P, _I64, _I32,
                            _P, _F32, _P, _P, _SZ, _P], _I32),
+    "msa_sparse_decode_noalloc": ([_P, _I32, _I32, _I32, _I32, ctypes.POINTER(_KV), _P, _I64, _I32, _P, _I64,
+                                   _I32, _P, _F32, _P, _P], _I32),
+    "msa_decode_noalloc_scratch_bytes": ([], _SZ),
     "msa_prefill_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_prefill": ([_P, _I32, _I32, _I32, ctypes.POINTER(_KV), _P, _I64, _I32, _P, _I64, _I32, _I32,
                             _P, _P, _F32, _P, _P, _SZ, _P], _I32),
@@ -285,6 +289,38 @@ def msa_sparse_decode(q, kv: KVCache, topk, block_table, seq_lens, softmax_scale
           _ptr(topk), topk.stride(0), topk.shape[1], _ptr(block_table), block_table.stride(0),
           block_table.shape[1], _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(dev))
+    return out
+
+
+def msa_sparse_decode_noalloc(q, kv: KVCache, topk, block_table, seq_lens, softmax_scale, *, out,
+                              decode_query_len=1):
+    """msa_sparse_decode with no workspace: the library's own per-GPU scratch
+    holds the split partials, and nothing is allocated (``out`` is required).
+    Calls that overlap in time on one GPU share that scratch and race."""
+    if topk.dim() == 3:
+        topk = topk[0]
+    _need_table_rows(block_table, seq_lens.shape[0], "block_table")
+    dev = q.device
+    _check_q(q)
+    _check_q(out, "out")
+    _need(topk, "topk", torch.int32, 2, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    if out.shape != q.shape or out.device != dev:
+        raise ValueError("out must have q's shape and device")
+    rows, hq, d = q.shape
+    if topk.shape[0] != rows:
+        raise ValueError(f"topk has {topk.shape[0]} rows, q has {rows}")
+    if d != kv.head_dim:
+        raise ValueError(f"q head_dim {d} != cache head_dim {kv.head_dim}")
+    num_reqs = seq_lens.shape[0]
+    if rows != num_reqs * decode_query_len:
+        raise ValueError(f"q has {rows} rows; {num_reqs} requests x decode_query_len {decode_query_len} "
+                         f"= {num_reqs * decode_query_len}")
+    kvs = kv._struct()
+    _call("msa_sparse_decode_noalloc", _ptr(q), MSA_BF16, num_reqs, decode_query_len, hq, ctypes.byref(kvs),
+          _ptr(topk), topk.stride(0), topk.shape[1], _ptr(block_table), block_table.stride(0),
+          block_table.shape[1], _ptr(seq_lens), float(softmax_scale), _ptr(out), _stream(dev))
     return out
 
 

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/msa.h"
 #include "msa_device.h"
@@ -358,6 +359,71 @@ MSA_API msa_status_t msa_sparse_decode(const void* q, int32_t q_dtype, int32_t n
                                        hipStream_t stream) {
   return decode_impl(true, q, q_dtype, num_reqs, decode_query_len, num_q_heads, kv, topk, topk_row_stride, topk_k,
                      block_table, bt_row_stride, bt_cols, seq_lens, softmax_scale, out, workspace, workspace_bytes,
+                     stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace: the split-K partials go to a fixed
+// device array instead.  With at least 512 (row, kv head) units the decode
+// runs one split and needs no scratch; below that it takes
+// ns = ceil(512 / units) splits (units * ns < 1024), and the partials of a
+// row head are (D + 2) fp32 per split, so a group of <= 16 query heads at
+// D <= 128 needs at most 1023 * 16 * 130 * 4 B + 256 B of alignment slack:
+// the array below is never too small for the split count the decode picks.
+// ---------------------------------------------------------------------------
+constexpr size_t kDecodeScratchBytes = size_t(9) << 20;
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The array's device address on the current device (host code must use this,
+// never the array's name, which is a host-side stand-in).
+msa_status_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+}  // namespace
+
+MSA_API size_t msa_decode_noalloc_scratch_bytes(void) { return kDecodeScratchBytes; }
+
+MSA_API msa_status_t msa_sparse_decode_noalloc(const void* q, int32_t q_dtype, int32_t num_reqs,
+                                               int32_t decode_query_len, int32_t num_q_heads,
+                                               const msa_kv_cache_t* kv, const int32_t* topk,
+                                               int64_t topk_row_stride, int32_t topk_k, const int32_t* block_table,
+                                               int64_t bt_row_stride, int32_t bt_cols, const int32_t* seq_lens,
+                                               float softmax_scale, void* out, hipStream_t stream) {
+  msa_status_t st = decode_impl(false, q, q_dtype, num_reqs, decode_query_len, num_q_heads, kv, topk,
+                                topk_row_stride, topk_k, block_table, bt_row_stride, bt_cols, seq_lens,
+                                softmax_scale, out, nullptr, 0, stream);
+  if (st != MSA_OK) return st;
+  const int64_t rows = (int64_t)num_reqs * decode_query_len;
+  if (rows == 0) return ok();
+  const int ns = choose_splits(rows, kv->num_kv_heads, topk_k, device_cus());
+  const size_t need = ns > 1 ? split_bytes(rows, num_q_heads, kv->head_dim, ns) : 0;
+  MSA_CHECK(need <= kDecodeScratchBytes, MSA_ERR_WORKSPACE_TOO_SMALL,
+            "decode of %lld rows x %d heads in %d splits needs %zu bytes of scratch; the library holds %zu "
+            "(use msa_sparse_decode with a workspace)",
+            (long long)rows, num_q_heads, ns, need, kDecodeScratchBytes);
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != MSA_OK) return st;
+  return decode_impl(true, q, q_dtype, num_reqs, decode_query_len, num_q_heads, kv, topk, topk_row_stride, topk_k,
+                     block_table, bt_row_stride, bt_cols, seq_lens, softmax_scale, out, ws, kDecodeScratchBytes,
                      stream);
 }
 

@@ -218,6 +218,32 @@ MSA_API msa_status_t msa_sparse_decode(
     float softmax_scale, void* out,
     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * msa_sparse_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, math and output as
+ * msa_sparse_decode given a full workspace; the split-K partials go to a
+ * fixed device array of msa_decode_noalloc_scratch_bytes() bytes that the
+ * library holds on each GPU until the process ends.  The call itself
+ * allocates nothing.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (other streams, other threads) race and
+ * must be serialised by the caller; calls on one stream are ordered.  A
+ * decode whose partials would not fit returns MSA_ERR_WORKSPACE_TOO_SMALL
+ * (with the split count the decode picks, <= 16 query heads per kv head and
+ * head_dim <= 128, they always fit).  The first call on a device looks the
+ * array up (hipGetSymbolAddress), so make it outside graph capture.
+ */
+MSA_API msa_status_t msa_sparse_decode_noalloc(
+    const void* q, int32_t q_dtype, int32_t num_reqs, int32_t decode_query_len, int32_t num_q_heads,
+    const msa_kv_cache_t* kv,
+    const int32_t* topk, int64_t topk_row_stride, int32_t topk_k,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t bt_cols,
+    const int32_t* seq_lens,
+    float softmax_scale, void* out, hipStream_t stream);
+
+/* Size of msa_sparse_decode_noalloc's per-device scratch array, in bytes. */
+MSA_API size_t msa_decode_noalloc_scratch_bytes(void);
+
 /* Bytes of workspace msa_sparse_prefill needs (0 today; reserved). */
 MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
                                           int32_t topk_k);
