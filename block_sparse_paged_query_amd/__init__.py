@@ -47,7 +47,9 @@ class MsaError(RuntimeError):
 
 
 def library_path():
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+    """The in-tree libmsa.so (MSA_LIBRARY names another build, e.g. the host
+    sanitizer copy the CPU tests load)."""
+    return os.environ.get("MSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
 
 class _KV(ctypes.Structure):
