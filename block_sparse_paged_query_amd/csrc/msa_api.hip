@@ -458,7 +458,7 @@ static msa_status_t prefill_impl(bool launch, const void* q, int32_t q_dtype, in
   a.num_reqs = num_reqs;
   a.dql = 1;
   a.total_rows = total_q;
-  if (msa::prefill_blocks_supported(a.group, kv->head_dim, fmt_of(kv->kv_dtype), bt_cols))
+  if (msa::prefill_blocks_supported(a.group, kv->head_dim, fmt_of(kv->kv_dtype)))
     return hip_status(msa::launch_prefill_blocks(a, fmt_of(kv->kv_dtype), stream), "prefill launch");
   return hip_status(msa::launch_attend_rows(a, fmt_of(kv->kv_dtype), msa::kModePrefill, total_q, stream),
                     "prefill launch");

@@ -55,9 +55,10 @@ struct AttendArgs {
 
 hipError_t launch_attend_rows(const AttendArgs& a, int fmt, int mode, int rows, hipStream_t stream);
 
-// Matrix-core prefill over query tiles (bf16, fp8 or NVFP4 pages, head_dim
-// 128, 8 or 16 query heads per kv head, block tables of at most 2048 columns).
-bool prefill_blocks_supported(int group, int head_dim, int fmt, int bt_cols);
+// Matrix-core prefill over query tiles: bf16, fp8 or NVFP4 pages; head_dim
+// 128 (or 64 for bf16 and fp8); 1, 2, 4, 8 or 16 query heads per kv head.
+// Other head groups take the row-wise kernel.
+bool prefill_blocks_supported(int group, int head_dim, int fmt);
 hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t stream);
 
 struct TableArgs {

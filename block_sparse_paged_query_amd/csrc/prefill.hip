@@ -10,11 +10,12 @@
 //      _write_sparse_block_table_row_from_values (the tokens a row sees).
 //
 // Work decomposition.  A workgroup (8 waves) owns one kv head and QT
-// consecutive query rows of one request (QT = 32 for 8 query heads per kv
-// head, 16 for 16).  Every query row picks its own blocks, so the workgroup
-// first builds, per block of the request, the bit mask of its rows that
-// selected it (and may see it causally), then walks the blocks some row
-// selected in ascending order.  Each such block's K and V (128 keys x 256 B)
+// consecutive query rows of one request (QT = 256 / G for G query heads per
+// kv head: 16 rows at G = 16, 256 at G = 1).  Every query row picks its own
+// blocks, so the workgroup first builds, per block of the request, the bit
+// mask of its rows that selected it (and may see it causally), then walks
+// the blocks some row selected in ascending order (a window of blocks at a
+// time for long contexts).  Each such block's K and V (128 keys x D bf16)
 // go once into LDS by direct-to-LDS buffer loads (a scalar descriptor per
 // block, 32-bit lane offsets; each lane's LDS slot is fixed, so layouts are
 // made by choosing which global chunk a lane fetches),
@@ -47,13 +48,21 @@ namespace msa {
 constexpr int kPfWaves = 8;                 // two per SIMD: one's softmax overlaps the other's MFMAs
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfTiles = 2;                 // matrix tiles per wave
-constexpr int kPfMaxBlocks = 2048;          // request blocks a workgroup can index
-constexpr int kPfBlockBytes = kBlockTokens * 256;   // one block of K (or V), bf16, head_dim 128
+// Row masks: a workgroup tile has QT = 16 * 16 / G rows (32 for 8 query heads
+// per kv head, 256 for 1), so a block's mask is MW = QT / 32 words; the block
+// masks of a window of kPfWindow<MW> blocks are held at once (a request with
+// more blocks is walked window by window).
+template <int MW>
+constexpr int kPfWindow = MW <= 2 ? 2048 : 4096 / MW;
+// one block of K (or V) in the compute layout: 128 keys x D bf16 / fp16
+template <int D>
+constexpr int kPfBlockBytes = kBlockTokens * 2 * D;
 // raw bytes of one block (one kv head, K and V) in the staging buffers
-constexpr int kPfFp8RawBytes = 2 * kBlockTokens * 128;               // [key][128] K, then [16-byte piece][key] V
+template <int D>
+constexpr int kPfFp8RawBytes = 2 * kBlockTokens * D;                  // [key][D] K, then [16-byte piece][key] V
 constexpr int kPfNvfp4RawBytes = kPagesPerBlock * 2 * 9 * 128;       // per page: K slot, V slot (1152 B each)
-template <int FMT>
-constexpr int kPfRawBytes = FMT == kFmtBf16 ? kPfBlockBytes : (FMT == kFmtFp8 ? kPfFp8RawBytes : kPfNvfp4RawBytes);
+template <int FMT, int D>
+constexpr int kPfRawBytes = FMT == kFmtBf16 ? kPfBlockBytes<D> : (FMT == kFmtFp8 ? kPfFp8RawBytes<D> : kPfNvfp4RawBytes);
 // compute operand type: bf16 for bf16 / fp8 pages, fp16 for NVFP4 pages
 template <int FMT> struct PfOp { typedef bf16x8 type; };
 template <> struct PfOp<kFmtNvfp4> { typedef f16x8 type; };
@@ -71,8 +80,9 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// K row swizzle: 16-byte chunk c of key row k sits at chunk c ^ (k & 15).
-__device__ __forceinline__ int k_swz(int key) { return key & 15; }
+// K row swizzle: 16-byte chunk c of key row k sits at chunk c ^ (k & (D/8 - 1)).
+template <int D>
+__device__ __forceinline__ int k_swz(int key) { return key & (D / 8 - 1); }
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -81,16 +91,19 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // (d = 8 lc .. 8 lc + 7) of key.
 
 // The copy of block `phys` (logical block `blk`), kv head kvh, into LDS
-// (kb, vb): four 16-byte K loads and four V loads per lane.  K unit
-// (wave, part) holds keys 16 wave + 4 part + lane / 16 (one page per wave),
-// V unit holds keys 32 part + lane / 2 (two pages) at d chunk
-// 2 wave + lane % 2, so every address is a per-block scalar base plus a small
-// per-lane offset (V: the same offset for all four parts).  Keys at or past
-// seq_len (only in a request's last block) are read from key 0 of the block
-// instead (finite data that gets probability zero), so no NaN of an
-// unwritten slot reaches the products.
+// (kb, vb): each wave copies one 16-token page of K and an eighth of V,
+// D / 32 instructions of 1 KB for each side.  K instruction (wave, part)
+// holds keys 16 wave + (64 / L) part + lane / L (L = D / 8 lanes per key
+// row); V instruction v = wave * (D / 32) + part holds keys 32 (v % 4) +
+// lane / 2 at d chunk 2 (v / 4) + lane % 2.  So every address is a per-block
+// scalar base plus a small per-lane offset.  Keys at or past seq_len (only
+// in a request's last block) are read from key 0 of the block instead
+// (finite data that gets probability zero), so no NaN of an unwritten slot
+// reaches the products.
+template <int D>
 __device__ __forceinline__ void pf_issue_block(lds_u8* kb, lds_u8* vb, const AttendArgs& a, int kvh, int phys,
                                                int blk, int seq_len) {
+  constexpr int L = D / 8, KPI = 64 / L, PARTS = D / 32;
   // (block ids come from LDS: make their uniformity explicit so that the
   // bases below are scalar and only 32-bit lane offsets stay in registers)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -101,47 +114,51 @@ __device__ __forceinline__ void pf_issue_block(lds_u8* kb, lds_u8* vb, const Att
   const int64_t boff = (int64_t)phys * a.blk_units * a.sub_stride + (int64_t)kvh * a.head_stride;
   const int rs = a.row_stride;
   const int nkeys = seq_len - blk * kBlockTokens;     // keys of this block that exist (>= 1)
-  const int kq = lane >> 4, kpc = lane & 15;          // K: key 16 wave + 4 part + kq, 16-byte chunk kpc
-  const int vq = lane >> 1, vlc = 2 * wave + (lane & 1);   // V: key 32 part + vq, chunk vlc
+  const int kq = lane / L, kpc = lane % L;            // K: key 16 wave + KPI part + kq, 16-byte chunk kpc
+  const int vq = lane >> 1, vodd = lane & 1;          // V: key 32 (v % 4) + vq, chunk 2 (v / 4) + vodd
   if (nkeys >= kBlockTokens && a.sub_stride < (int64_t(1) << 27)) {
     // scalar buffer descriptors over the wave's K page and the block's V
-    // pages; lanes add 32-bit offsets (V parts: a scalar offset per part)
+    // pages; lanes add 32-bit offsets (V: a scalar offset per instruction)
     const int vspan = (int)(7 * a.sub_stride) + kPageTokens * rs;
     const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.k_base + boff + wave * a.sub_stride), (short)0, kPageTokens * rs, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t vr_ =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_base + boff), (short)0, vspan, kRawBufferWord3);
-    const int voff = (vq >> 4) * (int)a.sub_stride + (vq & 15) * rs + (vlc << 4);
+    const int voff = (vq >> 4) * (int)a.sub_stride + (vq & 15) * rs + (vodd << 4);
 #pragma unroll
-    for (int part = 0; part < 4; ++part) {
-      const int kr = 4 * part + kq;                   // key within the wave's page
-      const int koff = kr * rs + ((kpc ^ k_swz(kr)) << 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr_, kb + (wave * 4 + part) * 1024, 16, koff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr_, vb + (wave * 4 + part) * 1024, 16, voff,
-                                               2 * part * (int)a.sub_stride, 0, 0);
+    for (int part = 0; part < PARTS; ++part) {
+      const int kr = KPI * part + kq;                 // key within the wave's page
+      const int koff = kr * rs + ((kpc ^ k_swz<D>(kr)) << 4);
+      const int v = wave * PARTS + part;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr_, kb + (wave * PARTS + part) * 1024, 16, koff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr_, vb + v * 1024, 16, voff,
+                                               2 * (v & 3) * (int)a.sub_stride + 32 * (v >> 2), 0, 0);
     }
   } else {
 #pragma unroll
-    for (int part = 0; part < 4; ++part) {
-      const int kkey = 16 * wave + 4 * part + kq, vkey = 32 * part + vq;
+    for (int part = 0; part < PARTS; ++part) {
+      const int v = wave * PARTS + part;
+      const int kkey = 16 * wave + KPI * part + kq, vkey = 32 * (v & 3) + vq;
       const int ks = kkey < nkeys ? kkey : 0, vs = vkey < nkeys ? vkey : 0;
-      __builtin_amdgcn_global_load_lds(a.k_base + boff + (ks >> 4) * a.sub_stride + (ks & 15) * rs +
-                                           ((kpc ^ k_swz(kkey)) << 4),
-                                       kb + (wave * 4 + part) * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.v_base + boff + (vs >> 4) * a.sub_stride + (vs & 15) * rs + (vlc << 4),
-                                       vb + (wave * 4 + part) * 1024, 16, 0, 0);
+      const int kcol = (kpc ^ k_swz<D>(kkey)) << 4;
+      __builtin_amdgcn_global_load_lds(a.k_base + boff + (ks >> 4) * a.sub_stride + (ks & 15) * rs + kcol,
+                                       kb + (wave * PARTS + part) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.v_base + boff + (vs >> 4) * a.sub_stride + (vs & 15) * rs +
+                                           ((2 * (v >> 2) + vodd) << 4),
+                                       vb + v * 1024, 16, 0, 0);
     }
   }
 }
 
-template <class OT>
+template <class OT, int D>
 struct PfWave {
-  static constexpr int KK = 4, NN = 8;
+  static constexpr int KK = D / 32, NN = D / 16;
   OT qop[kPfTiles][KK];
   f32x4 acc[kPfTiles][NN];
   f32x4 lacc[kPfTiles];   // softmax denominators: P times an all-ones operand
   float m[kPfTiles];
   int lrow[kPfTiles];     // row within the workgroup tile, or -1
+  int lbit[kPfTiles];     // its bit in the wave's block mask
   int lpos[kPfTiles];     // that row's absolute position
 };
 
@@ -162,11 +179,11 @@ constexpr float kLazy = 8.f;
 // chunk's once this chunk's products have consumed them, so those LDS reads
 // overlap this chunk's softmax and PV work instead of stalling the next
 // chunk's first product.
-template <int MASK, class OT, class PT, class NextK, class NextV>
-__device__ __forceinline__ void pf_chunk(PfWave<OT>& w, OT (&kop)[2][PfWave<OT>::KK], PT (&vop)[PfWave<OT>::NN],
-                                         const float (&bias)[kPfTiles], const PT& ones, float sl2, bool causal,
-                                         int kbase, NextK&& next_k, NextV&& next_v) {
-  constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
+template <int MASK, int D, class OT, class PT, class NextK, class NextV>
+__device__ __forceinline__ void pf_chunk(PfWave<OT, D>& w, OT (&kop)[2][PfWave<OT, D>::KK],
+                                         PT (&vop)[PfWave<OT, D>::NN], const float (&bias)[kPfTiles], const PT& ones,
+                                         float sl2, bool causal, int kbase, NextK&& next_k, NextV&& next_v) {
+  constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN;
   constexpr bool kF16 = __is_same(PT, f16x8);
   float sv[kPfTiles][8];
 #pragma unroll
@@ -252,18 +269,18 @@ struct PfNext {       // the block whose copies are issued during this one
 // The block's four 32-key chunks against the tiles in MASK.  Each chunk's K
 // and V operands (shared by the wave's active tiles) are read from LDS while
 // the previous chunk computes.
-template <int MASK, class OT, class PT>
-__device__ __forceinline__ void pf_chunks(PfWave<OT>& w, const uint8_t* kb, const uint8_t* vb,
-                                          const int (&koff)[PfWave<OT>::KK], int voff,
+template <int MASK, int D, class OT, class PT>
+__device__ __forceinline__ void pf_chunks(PfWave<OT, D>& w, const uint8_t* kb, const uint8_t* vb,
+                                          const int (&koff)[PfWave<OT, D>::KK], int voff,
                                           const float (&bias)[kPfTiles], const PT& ones, float sl2, bool causal,
                                           int kbase0) {
-  constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
+  constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN;
   auto load_k = [&](OT (&kop)[2][KK], int c) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        kop[tt][kk] = *reinterpret_cast<const OT*>(kb + (c * 32 + 16 * tt) * 256 + koff[kk]);
+        kop[tt][kk] = *reinterpret_cast<const OT*>(kb + (c * 32 + 16 * tt) * (2 * D) + koff[kk]);
   };
   auto load_v = [&](PT (&vop)[NN], int c) {
 #pragma unroll
@@ -282,29 +299,30 @@ __device__ __forceinline__ void pf_chunks(PfWave<OT>& w, const uint8_t* kb, cons
   load_v(vop, 0);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    pf_chunk<MASK, OT, PT>(w, kop, vop, bias, ones, sl2, causal, kbase0 + c * 32,
+    pf_chunk<MASK, D, OT, PT>(w, kop, vop, bias, ones, sl2, causal, kbase0 + c * 32,
                        [&](OT (&k)[2][KK]) { if (c < 3) load_k(k, c + 1); },
                        [&](PT (&v)[NN]) { if (c < 3) load_v(v, c + 1); });
   }
 }
 
-// One selected block against this wave's tiles.  `causal` is set when the
-// block can be the own block of a row of this workgroup (keys past a row's
-// position must be masked); earlier blocks need only the row selection.
-// Every wave first issues its pieces of the next block's copies, active or
-// not.
-template <class OT, class PT>
-__device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* kb, const uint8_t* vb, uint32_t bmask,
-                                                 int blk, int wave, int RT, float sl2, bool causal,
+// One selected block against this wave's tiles.  `bmask` holds the wave's
+// rows that selected the block (bit i * RT + k: row k of tile i).  `causal`
+// is set when the block can be the own block of a row of this workgroup
+// (keys past a row's position must be masked); earlier blocks need only the
+// row selection.  Every wave first issues its pieces of the next block's
+// copies, active or not.
+template <int D, class OT, class PT>
+__device__ __forceinline__ void pf_compute_block(PfWave<OT, D>& w, const uint8_t* kb, const uint8_t* vb,
+                                                 uint32_t bmask, int blk, int RT, float sl2, bool causal,
                                                  const PfNext& nx, const AttendArgs& a, int kvh, int seq_len) {
-  constexpr int KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
+  constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN;
   constexpr bool kF16 = __is_same(PT, f16x8);
   static_assert(kPfTiles == 2, "the tile sets below enumerate two tiles");
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   // per-lane LDS offsets (chunk / tile / step parts are compile-time)
   int koff[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) koff[kk] = r * 256 + (((4 * kk + g) ^ r) << 4);
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = r * (2 * D) + (((4 * kk + g) ^ k_swz<D>(r)) << 4);
   // transposing read of lane (j, g): key 4g + j/4 (+16 hh) of the chunk, the
   // 8 bytes at d = 16 nn + 4 (j % 4)
   const int voff = g * 128 + (r >> 2) * 32 + (r & 3) * 8;
@@ -314,18 +332,18 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* k
   int tiles = 0;
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
-    const uint32_t tile_bits = ((1u << RT) - 1u) << ((wave * kPfTiles + i) * RT);
+    const uint32_t tile_bits = (uint32_t)((1ull << RT) - 1ull) << (i * RT);
     tiles |= (bmask & tile_bits) ? (1 << i) : 0;
-    const bool sel = w.lrow[i] >= 0 && ((bmask >> w.lrow[i]) & 1u);
+    const bool sel = w.lrow[i] >= 0 && ((bmask >> w.lbit[i]) & 1u);
     bias[i] = sel ? 0.f : -INFINITY;
   }
   const int kpos_blk = blk * kBlockTokens;
   const uint32_t one2 = kF16 ? 0x3c003c00u : 0x3f803f80u;   // 1.0 x 2 in the operand type
   const PT ones = __builtin_bit_cast(PT, u32x4{one2, one2, one2, one2});
-  if (nx.valid) pf_issue_block(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len);
-  if (tiles == 3) pf_chunks<3, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
-  else if (tiles == 1) pf_chunks<1, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
-  else if (tiles == 2) pf_chunks<2, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  if (nx.valid) pf_issue_block<D>(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len);
+  if (tiles == 3) pf_chunks<3, D, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  else if (tiles == 1) pf_chunks<1, D, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  else if (tiles == 2) pf_chunks<2, D, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
 }
 
 // ---- staged formats -------------------------------------------------------
@@ -333,13 +351,14 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT>& w, const uint8_t* k
 // Copy of one block's raw bytes (kv head kvh) into the staging buffer `raw`,
 // spread over the workgroup: each wave instruction fills 64 consecutive
 // 16-byte slots, a lane's source being any 16-byte piece.
-//   fp8:   K as [key][128 B] (piece (key, n) at key * 8 + n), then V as
-//          [n][key] (piece at 1024 + n * 128 + key) so that the conversion
+//   fp8:   K as [key][D B] (piece (key, n) at key * D / 16 + n), then V as
+//          [n][key] (piece 8 D + n * 128 + key) so that the conversion
 //          writes the V layout with consecutive lanes on consecutive keys.
 //   NVFP4: the block's 8 pages, each the K slot then the V slot of kvh
-//          (2 x 1152 B, adjacent in the page), piece q at q.
-template <int FMT>
+//          (2 x 1152 B, adjacent in the page), piece q at q (head_dim 128).
+template <int FMT, int D>
 __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a, int kvh, int phys) {
+  constexpr int NPK = D / 16, HALF = kBlockTokens * NPK;   // pieces per key row; K pieces
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));   // recompute the lane offsets here rather than keep them live across blocks
@@ -355,11 +374,12 @@ __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a,
       const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_base + boff),
                                                                            (short)0, span, kRawBufferWord3);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 2 * HALF / kPfThreads; ++k) {
         const int q = k * kPfThreads + wave * 64 + lane;
-        const int key = k < 2 ? q >> 3 : (q - 1024) & 127, n = k < 2 ? q & 7 : (q - 1024) >> 7;
+        const bool vs = k >= HALF / kPfThreads;
+        const int key = vs ? (q - HALF) & 127 : q / NPK, n = vs ? (q - HALF) >> 7 : q % NPK;
         const int off = (key >> 4) * sub + (key & 15) * rs + 16 * n;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(k < 2 ? kr_ : vr_, raw + (k * kPfThreads + wave * 64) * 16, 16, off,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vs ? vr_ : kr_, raw + (k * kPfThreads + wave * 64) * 16, 16, off,
                                                  0, 0, 0);
       }
     } else {
@@ -379,14 +399,14 @@ __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a,
   if constexpr (FMT == kFmtFp8) {
     const int rs = a.row_stride;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 2 * HALF / kPfThreads; ++k) {
       const int q = k * kPfThreads + wave * 64 + lane;
       const uint8_t* src;
-      if (k < 2) {
-        const int key = q >> 3, n = q & 7;
+      if (k < HALF / kPfThreads) {
+        const int key = q / NPK, n = q % NPK;
         src = a.k_base + boff + (key >> 4) * a.sub_stride + (key & 15) * rs + 16 * n;
       } else {
-        const int q2 = q - 1024, n = q2 >> 7, key = q2 & 127;
+        const int q2 = q - HALF, n = q2 >> 7, key = q2 & 127;
         src = a.v_base + boff + (key >> 4) * a.sub_stride + (key & 15) * rs + 16 * n;
       }
       __builtin_amdgcn_global_load_lds(src, raw + (k * kPfThreads + wave * 64) * 16, 16, 0, 0);
@@ -409,11 +429,12 @@ __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a,
 // item (key, n) is the 16 elements d = 16 n .. 16 n + 15, i.e. chunks 2n and
 // 2n + 1.  Keys at or past `nkeys` (the request's end, in its last block)
 // become zeros, which the causal mask gives probability zero.
-template <int FMT>
+template <int FMT, int D>
 __device__ __forceinline__ void pf_stage_item(const uint8_t* raw, bool v_side, int key, int n, uint32_t out[8]) {
   if constexpr (FMT == kFmtFp8) {
     // K -> bf16 (the QK^T operand type), V -> fp16 (the PV operand type)
-    const u32x4 w = *reinterpret_cast<const u32x4*>(raw + (v_side ? 16384 + (n * 128 + key) * 16 : key * 128 + 16 * n));
+    const u32x4 w =
+        *reinterpret_cast<const u32x4*>(raw + (v_side ? kBlockTokens * D + (n * 128 + key) * 16 : key * D + 16 * n));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = v_side ? f16x2_bits(fp8x2_to_f16x2<false>(w[i])) : fp8x2_to_bf16x2<false>(w[i]);
@@ -438,27 +459,28 @@ __device__ __forceinline__ void pf_stage_item(const uint8_t* raw, bool v_side, i
   }
 }
 
-template <int FMT>
+template <int FMT, int D>
 __device__ __forceinline__ void pf_stage_convert(const uint8_t* raw, uint8_t* kc, uint8_t* vc, int nkeys) {
+  constexpr int NPK = D / 16, HALF = kBlockTokens * NPK;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));    // as in the copy issue: offsets recomputed per block
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 2 * HALF / kPfThreads; ++k) {
     const int q = k * kPfThreads + tid;
-    const bool v_side = k >= 2;
-    const int key = v_side ? ((q - 1024) & 127) : (q >> 3);
-    const int n = v_side ? ((q - 1024) >> 7) : (q & 7);
+    const bool v_side = k >= HALF / kPfThreads;
+    const int key = v_side ? ((q - HALF) & 127) : (q / NPK);
+    const int n = v_side ? ((q - HALF) >> 7) : (q % NPK);
     uint32_t o[8];
-    pf_stage_item<FMT>(raw, v_side, key, n, o);
+    pf_stage_item<FMT, D>(raw, v_side, key, n, o);
     if (key >= nkeys) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = 0u;
     }
     const u32x4 c0 = {o[0], o[1], o[2], o[3]}, c1 = {o[4], o[5], o[6], o[7]};
     if (!v_side) {
-      const int sw = key & 15;   // chunk c of the key row sits at c ^ (key & 15)
-      *reinterpret_cast<u32x4*>(kc + key * 256 + (((2 * n) ^ sw) << 4)) = c0;
-      *reinterpret_cast<u32x4*>(kc + key * 256 + (((2 * n + 1) ^ sw) << 4)) = c1;
+      const int sw = k_swz<D>(key);   // chunk c of the key row sits at c ^ sw
+      *reinterpret_cast<u32x4*>(kc + key * (2 * D) + (((2 * n) ^ sw) << 4)) = c0;
+      *reinterpret_cast<u32x4*>(kc + key * (2 * D) + (((2 * n + 1) ^ sw) << 4)) = c1;
     } else {
       *reinterpret_cast<u32x4*>(vc + (n * 128 + key) * 32) = c0;
       *reinterpret_cast<u32x4*>(vc + (n * 128 + key) * 32 + 16) = c1;
@@ -466,20 +488,20 @@ __device__ __forceinline__ void pf_stage_convert(const uint8_t* raw, uint8_t* kc
   }
 }
 
-template <int FMT>
+template <int FMT, int D, int MW>
 __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const AttendArgs a, int n_slots) {
   typedef typename PfOp<FMT>::type OT;
   typedef typename PfPv<FMT>::type PT;
-  constexpr int D = 128, KK = PfWave<OT>::KK, NN = PfWave<OT>::NN;
+  constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN, WIN = kPfWindow<MW>;
   // Four LDS buffers as distinct objects: the loops below are unrolled by two,
   // so the compiler knows the in-flight copies target another buffer.
   //   bf16:        K / V double buffers (bA, bC) and (bB, bD)
   //   fp8 / NVFP4: compute K, V (bA, bB) and raw staging buffers bC, bD
-  __shared__ __align__(16) uint8_t bA[kPfBlockBytes], bB[kPfBlockBytes];
-  __shared__ __align__(16) uint8_t bC[kPfRawBytes<FMT>], bD[kPfRawBytes<FMT>];
-  __shared__ uint32_t s_mask[kPfMaxBlocks];
-  __shared__ uint16_t s_list[kPfMaxBlocks];   // selected blocks, ascending
-  __shared__ int32_t s_phys[kPfMaxBlocks];    // their physical block ids
+  __shared__ __align__(16) uint8_t bA[kPfBlockBytes<D>], bB[kPfBlockBytes<D>];
+  __shared__ __align__(16) uint8_t bC[kPfRawBytes<FMT, D>], bD[kPfRawBytes<FMT, D>];
+  __shared__ uint32_t s_mask[WIN][MW];        // per block of the window: its selecting rows
+  __shared__ uint16_t s_list[WIN];            // selected blocks of the window, ascending
+  __shared__ int32_t s_phys[WIN];             // their physical block ids
   __shared__ int s_info[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -552,47 +574,18 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   const int pos_last = ctx0 + (row_end - 1 - cu0);
   const int nblk = pos_last < 0 ? 0 : min(pos_last / kBlockTokens + 1, a.bt_cols);
   const int32_t* bt_row = a.block_table + (int64_t)req * a.bt_stride;
-
-  // ---- per-block masks of the rows that selected the block (and may see it)
-  for (int j = tid; j < nblk; j += kPfThreads) s_mask[j] = 0u;
-  __syncthreads();
   const int nrows = row_end - row0;
-  for (int idx = tid; idx < nrows * a.topk_k; idx += kPfThreads) {
-    const int rr = idx / a.topk_k, tk = idx - rr * a.topk_k;
-    const int pos = pos_first + rr;
-    const int blk = a.topk[(int64_t)(row0 + rr) * a.topk_stride + tk];
-    if (pos >= 0 && blk >= 0 && blk <= pos / kBlockTokens && blk < nblk) atomicOr(&s_mask[blk], 1u << rr);
-  }
-  __syncthreads();
-  // ---- selected blocks, ascending (blocks whose pages lie outside the cache are skipped)
-  if (wave == 0) {
-    int n = 0;
-    for (int base = 0; base < nblk; base += 64) {
-      const int j = base + lane;
-      bool act = j < nblk && s_mask[j] != 0u;
-      if (act) {
-        const int phys = bt_row[j];
-        const int64_t last = (int64_t)phys * a.blk_units + a.v_unit_offset + kPagesPerBlock - 1;
-        act = phys >= 0 && last < a.num_units;
-      }
-      const uint64_t am = __ballot(act);
-      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(am >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)am, 0u));
-      if (act) {
-        s_list[n + rank] = (uint16_t)j;
-        s_phys[n + rank] = bt_row[j];
-      }
-      n += __popcll(am);
-    }
-    if (lane == 0) s_info[0] = n;
-  }
 
-  // ---- this wave's query operands and row data
-  PfWave<OT> w;
+  // ---- this wave's query operands and row data.  The wave's rows are
+  // 2 RT consecutive ones, bits [wbit0, wbit0 + 2 RT) of a block's mask.
+  PfWave<OT, D> w;
+  const int wbit0 = wave * kPfTiles * RT;
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
     const int rr = (wave * kPfTiles + i) * RT + r / G;
     const bool ok = r < RT * G && rr < nrows;
     w.lrow[i] = ok ? rr : -1;
+    w.lbit[i] = rr - wbit0;
     w.lpos[i] = pos_first + rr;
     w.m[i] = -INFINITY;
     w.lacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -611,68 +604,111 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   }
   const float kscale = a.k_scale ? *a.k_scale : 1.f;
   const float sl2 = a.softmax_scale * kscale * kLog2e;
-  __syncthreads();
-  const int n_act = s_info[0];
-
-  const uint32_t wave_bits = ((1u << (kPfTiles * RT)) - 1u) << (wave * kPfTiles * RT);
+  const int wword = wbit0 >> 5, wshift = wbit0 & 31;
+  const uint32_t wave_bits = (uint32_t)((1ull << (kPfTiles * RT)) - 1ull);
   const int own_first = pos_first / kBlockTokens;   // blocks before it are wholly in every row's past
-  if constexpr (FMT == kFmtBf16) {
-    lds_u8 *k0 = (lds_u8*)bA, *k1 = (lds_u8*)bB, *v0 = (lds_u8*)bC, *v1 = (lds_u8*)bD;
-    if (n_act > 0) {
-      pf_issue_block(k0, v0, a, kvh, s_phys[0], s_list[0], seq_len);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- the request's blocks, a window of WIN at a time (one window unless
+  // the rows reach past WIN blocks); the softmax state carries across windows
+  for (int w0 = 0; w0 < nblk; w0 += WIN) {
+    const int w1 = min(w0 + WIN, nblk);
+    if (w0 > 0) __syncthreads();   // every wave is done with the previous window's tables and buffers
+    // per-block masks of the rows that selected the block (and may see it)
+    for (int jj = tid; jj < (w1 - w0) * MW; jj += kPfThreads) s_mask[jj / MW][jj % MW] = 0u;
     __syncthreads();
-    for (int it = 0; it < n_act; it += 2) {
-      // even step: block in (k0, v0); the next one goes to (k1, v1)
-      {
-        const int j = s_list[it];
-        const PfNext nx = {k1, v1, it + 1 < n_act ? s_phys[it + 1] : 0, it + 1 < n_act ? (int)s_list[it + 1] : 0,
-                           it + 1 < n_act};
-        const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-        pf_compute_block<OT, PT>(w, bA, bC, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
-        __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
-        __syncthreads();
-      }
-      if (it + 1 >= n_act) break;
-      // odd step: block in (k1, v1); the next one goes to (k0, v0)
-      {
-        const int j = s_list[it + 1];
-        const PfNext nx = {k0, v0, it + 2 < n_act ? s_phys[it + 2] : 0, it + 2 < n_act ? (int)s_list[it + 2] : 0,
-                           it + 2 < n_act};
-        const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-        pf_compute_block<OT, PT>(w, bB, bD, bmask, j, wave, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
+    for (int idx = tid; idx < nrows * a.topk_k; idx += kPfThreads) {
+      const int rr = idx / a.topk_k, tk = idx - rr * a.topk_k;
+      const int pos = pos_first + rr;
+      const int blk = a.topk[(int64_t)(row0 + rr) * a.topk_stride + tk];
+      if (pos >= 0 && blk >= w0 && blk < w1 && blk <= pos / kBlockTokens)
+        atomicOr(&s_mask[blk - w0][rr >> 5], 1u << (rr & 31));
     }
-  } else {
-    // staged: raw block in bC / bD (alternating), converted into (bA, bB)
-    const PfNext none = {nullptr, nullptr, 0, 0, false};
-    if (n_act > 0) pf_stage_issue<FMT>((lds_u8*)bC, a, kvh, s_phys[0]);
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int it = 0; it < n_act; it += 2) {
-      {
-        const int j = s_list[it];
-        pf_stage_convert<FMT>(bC, bA, bB, seq_len - j * kBlockTokens);
-        __syncthreads();
-        if (it + 1 < n_act) pf_stage_issue<FMT>((lds_u8*)bD, a, kvh, s_phys[it + 1]);
-        const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-        pf_compute_block<OT, PT>(w, bA, bB, bmask, j, wave, RT, sl2, j >= own_first, none, a, kvh, seq_len);
-        __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
-        __syncthreads();                 // and every wave is done with (bA, bB)
+    // selected blocks, ascending (blocks whose pages lie outside the cache are skipped)
+    if (wave == 0) {
+      int n = 0;
+      for (int base = w0; base < w1; base += 64) {
+        const int j = base + lane;
+        bool act = false;
+        if (j < w1) {
+#pragma unroll
+          for (int mw = 0; mw < MW; ++mw) act |= s_mask[j - w0][mw] != 0u;
+        }
+        if (act) {
+          const int phys = bt_row[j];
+          const int64_t last = (int64_t)phys * a.blk_units + a.v_unit_offset + kPagesPerBlock - 1;
+          act = phys >= 0 && last < a.num_units;
+        }
+        const uint64_t am = __ballot(act);
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(am >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)am, 0u));
+        if (act) {
+          s_list[n + rank] = (uint16_t)(j - w0);
+          s_phys[n + rank] = bt_row[j];
+        }
+        n += __popcll(am);
       }
-      if (it + 1 >= n_act) break;
-      {
-        const int j = s_list[it + 1];
-        pf_stage_convert<FMT>(bD, bA, bB, seq_len - j * kBlockTokens);
-        __syncthreads();
-        if (it + 2 < n_act) pf_stage_issue<FMT>((lds_u8*)bC, a, kvh, s_phys[it + 2]);
-        const uint32_t bmask = __builtin_amdgcn_readfirstlane(s_mask[j]) & wave_bits;
-        pf_compute_block<OT, PT>(w, bA, bB, bmask, j, wave, RT, sl2, j >= own_first, none, a, kvh, seq_len);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+      if (lane == 0) s_info[0] = n;
+    }
+    __syncthreads();
+    const int n_act = s_info[0];
+    auto wave_mask = [&](int jl) -> uint32_t {
+      return (__builtin_amdgcn_readfirstlane(s_mask[jl][wword]) >> wshift) & wave_bits;
+    };
+
+    if constexpr (FMT == kFmtBf16) {
+      lds_u8 *k0 = (lds_u8*)bA, *k1 = (lds_u8*)bB, *v0 = (lds_u8*)bC, *v1 = (lds_u8*)bD;
+      if (n_act > 0) {
+        pf_issue_block<D>(k0, v0, a, kvh, s_phys[0], w0 + s_list[0], seq_len);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      for (int it = 0; it < n_act; it += 2) {
+        // even step: block in (k0, v0); the next one goes to (k1, v1)
+        {
+          const int jl = s_list[it], j = w0 + jl;
+          const PfNext nx = {k1, v1, it + 1 < n_act ? s_phys[it + 1] : 0,
+                             it + 1 < n_act ? w0 + (int)s_list[it + 1] : 0, it + 1 < n_act};
+          pf_compute_block<D, OT, PT>(w, bA, bC, wave_mask(jl), j, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
+          __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
+          __syncthreads();
+        }
+        if (it + 1 >= n_act) break;
+        // odd step: block in (k1, v1); the next one goes to (k0, v0)
+        {
+          const int jl = s_list[it + 1], j = w0 + jl;
+          const PfNext nx = {k0, v0, it + 2 < n_act ? s_phys[it + 2] : 0,
+                             it + 2 < n_act ? w0 + (int)s_list[it + 2] : 0, it + 2 < n_act};
+          pf_compute_block<D, OT, PT>(w, bB, bD, wave_mask(jl), j, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+        }
+      }
+    } else {
+      // staged: raw block in bC / bD (alternating), converted into (bA, bB)
+      const PfNext none = {nullptr, nullptr, 0, 0, false};
+      if (n_act > 0) pf_stage_issue<FMT, D>((lds_u8*)bC, a, kvh, s_phys[0]);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      for (int it = 0; it < n_act; it += 2) {
+        {
+          const int jl = s_list[it], j = w0 + jl;
+          pf_stage_convert<FMT, D>(bC, bA, bB, seq_len - j * kBlockTokens);
+          __syncthreads();
+          if (it + 1 < n_act) pf_stage_issue<FMT, D>((lds_u8*)bD, a, kvh, s_phys[it + 1]);
+          pf_compute_block<D, OT, PT>(w, bA, bB, wave_mask(jl), j, RT, sl2, j >= own_first, none, a, kvh, seq_len);
+          __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of the next block have landed
+          __syncthreads();                 // and every wave is done with (bA, bB)
+        }
+        if (it + 1 >= n_act) break;
+        {
+          const int jl = s_list[it + 1], j = w0 + jl;
+          pf_stage_convert<FMT, D>(bD, bA, bB, seq_len - j * kBlockTokens);
+          __syncthreads();
+          if (it + 2 < n_act) pf_stage_issue<FMT, D>((lds_u8*)bC, a, kvh, s_phys[it + 2]);
+          pf_compute_block<D, OT, PT>(w, bA, bB, wave_mask(jl), j, RT, sl2, j >= own_first, none, a, kvh, seq_len);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+        }
       }
     }
   }
@@ -714,8 +750,8 @@ __global__ __launch_bounds__(kPfThreads) void gather_dequant_prefill_kernel(cons
                                                                             int width_tokens, float* __restrict__ k_out,
                                                                             float* __restrict__ v_out) {
   constexpr int D = 128;
-  __shared__ __align__(16) uint8_t bK[FMT == kFmtBf16 ? kPfBlockBytes : 16];
-  __shared__ __align__(16) uint8_t bV[FMT == kFmtBf16 ? kPfBlockBytes : kPfRawBytes<FMT>];
+  __shared__ __align__(16) uint8_t bK[FMT == kFmtBf16 ? kPfBlockBytes<D> : 16];
+  __shared__ __align__(16) uint8_t bV[FMT == kFmtBf16 ? kPfBlockBytes<D> : kPfRawBytes<FMT, D>];
   const int tid = threadIdx.x;
   const int nslot = width_tokens / kBlockTokens;
   const int slot = blockIdx.x % nslot;
@@ -731,9 +767,9 @@ __global__ __launch_bounds__(kPfThreads) void gather_dequant_prefill_kernel(cons
   float* vb = v_out + ((row * width_tokens + slot * kBlockTokens) * a.num_kv_heads + kvh) * D;
   if (inside) {   // uniform
     if constexpr (FMT == kFmtBf16) {
-      pf_issue_block((lds_u8*)bK, (lds_u8*)bV, a, kvh, phys, 0, nkeys);
+      pf_issue_block<D>((lds_u8*)bK, (lds_u8*)bV, a, kvh, phys, 0, nkeys);
     } else {
-      pf_stage_issue<FMT>((lds_u8*)bV, a, kvh, phys);
+      pf_stage_issue<FMT, D>((lds_u8*)bV, a, kvh, phys);
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -750,7 +786,7 @@ __global__ __launch_bounds__(kPfThreads) void gather_dequant_prefill_kernel(cons
       for (int h = 0; h < 2; ++h) {
         const int c = 2 * n + h;
         const uint8_t* src = v_side ? bV + (((c >> 1) * kBlockTokens + key) * 2 + (c & 1)) * 16
-                                    : bK + key * 256 + ((c ^ k_swz(key)) << 4);
+                                    : bK + key * 256 + ((c ^ k_swz<D>(key)) << 4);
         const u32x4 w = *reinterpret_cast<const u32x4*>(src);
         o[4 * h + 0] = w[0];
         o[4 * h + 1] = w[1];
@@ -758,7 +794,7 @@ __global__ __launch_bounds__(kPfThreads) void gather_dequant_prefill_kernel(cons
         o[4 * h + 3] = w[3];
       }
     } else {
-      pf_stage_item<FMT>(bV, v_side, key, n, o);
+      pf_stage_item<FMT, D>(bV, v_side, key, n, o);
     }
     const bool keep = inside && key < nkeys;
     float* dst = (v_side ? vb : kb) + (int64_t)key * tok_stride + 16 * n;
@@ -798,25 +834,38 @@ hipError_t launch_gather_dequant_prefill(const AttendArgs& a, int fmt, const int
   return hipGetLastError();
 }
 
+template <int FMT, int D>
+static hipError_t launch_pf(const AttendArgs& a, dim3 grid, int n_slots, hipStream_t stream) {
+  switch (a.group) {
+    case 16:
+    case 8: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 1>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
+    case 4: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 2>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
+    case 2: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 4>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
+    default: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 8>), grid, dim3(kPfThreads), 0, stream, a, n_slots);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t stream) {
   const int QT = kPfWaves * kPfTiles * (16 / a.group);
   // tiles: ceil(rows / QT) per request and per padding range (before the
   // first request, after the last) is at most ceil(total / QT) + R + 2
   const int n_slots = (a.total_rows + QT - 1) / QT + a.num_reqs + 2;
-  const int64_t blocks = (int64_t)n_slots * a.num_kv_heads;
-  if (fmt == kFmtBf16) {
-    hipLaunchKernelGGL(prefill_blocks_kernel<kFmtBf16>, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a, n_slots);
-  } else if (fmt == kFmtFp8) {
-    hipLaunchKernelGGL(prefill_blocks_kernel<kFmtFp8>, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a, n_slots);
-  } else {
-    hipLaunchKernelGGL(prefill_blocks_kernel<kFmtNvfp4>, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a,
-                       n_slots);
+  const dim3 grid((unsigned)((int64_t)n_slots * a.num_kv_heads));
+  if (a.head_dim == 128) {
+    if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 128>(a, grid, n_slots, stream);
+    if (fmt == kFmtFp8) return launch_pf<kFmtFp8, 128>(a, grid, n_slots, stream);
+    return launch_pf<kFmtNvfp4, 128>(a, grid, n_slots, stream);
   }
-  return hipGetLastError();
+  if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 64>(a, grid, n_slots, stream);
+  return launch_pf<kFmtFp8, 64>(a, grid, n_slots, stream);
 }
 
-bool prefill_blocks_supported(int group, int head_dim, int fmt, int bt_cols) {
-  return (group == 8 || group == 16) && head_dim == 128 && bt_cols <= kPfMaxBlocks;
+// Query groups that divide a 16-column tile into whole rows; head_dim 64 or
+// 128 (NVFP4: 128); any block-table width (windows of blocks).
+bool prefill_blocks_supported(int group, int head_dim, int fmt) {
+  const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
+  return g_ok && (head_dim == 128 || (head_dim == 64 && fmt != kFmtNvfp4));
 }
 
 }  // namespace msa

@@ -227,8 +227,13 @@ def test_prefill_parity_small():
 
 @pytest.mark.parametrize("kw", [
     dict(Hq=32, Hkv=2, seed=41),                         # 16 query heads per kv head
-    dict(Hq=16, Hkv=4, seed=42),                         # 4 per kv head: row-wise path
-    dict(D=64, Hq=16, Hkv=2, seed=43),                   # head_dim 64: row-wise path
+    dict(Hq=16, Hkv=4, seed=42),                         # 4 per kv head: two mask words
+    dict(D=64, Hq=16, Hkv=2, seed=43),                   # head_dim 64
+    dict(Hq=4, Hkv=4, seed=57),                          # 1 per kv head: eight mask words
+    dict(Hq=8, Hkv=4, seed=58),                          # 2 per kv head: four mask words
+    dict(D=64, Hq=8, Hkv=8, kv_dtype="fp8", seed=59),    # head_dim 64, fp8 pages, 1 per kv head
+    dict(Hq=12, Hkv=4, seed=60),                         # 3 per kv head: row-wise kernel
+    dict(Hq=12, Hkv=2, kv_dtype="nvfp4", seed=62),       # 6 per kv head: row-wise kernel
     dict(block_page_stride=16, seed=44),                 # K and V sides in one block
     dict(qlens=[1, 40, 700], context=[3000, 0, 129], seed=45),   # long context, tiny request
     dict(qlens=[0, 300], context=[50, 0], seed=46),      # an empty request
@@ -240,8 +245,9 @@ def test_prefill_parity_small():
     dict(kv_dtype="fp8", block_page_stride=16, seed=50),
     dict(kv_dtype="nvfp4", qlens=[1, 40, 700], context=[3000, 0, 129], seed=51),
     dict(kv_dtype="fp8", qlens=[0, 300], context=[50, 0], seed=54),
-    dict(kv_dtype="fp8", Hq=16, Hkv=4, seed=52),         # 4 per kv head: row-wise path
-    dict(kv_dtype="nvfp4", Hq=16, Hkv=4, seed=55),       # 4 per kv head: row-wise path
+    dict(kv_dtype="fp8", Hq=16, Hkv=4, seed=52),         # 4 per kv head
+    dict(kv_dtype="nvfp4", Hq=16, Hkv=4, seed=55),       # 4 per kv head
+    dict(kv_dtype="nvfp4", Hq=2, Hkv=1, seed=63),        # 2 per kv head
     dict(selection="per_block", seed=56),                # rows of one block share their top-k row
 ])
 def test_prefill_parity_variants(kw):
@@ -281,9 +287,9 @@ def test_prefill_parity_full_size(kv_dtype, selection, every_row):
 
 @pytest.mark.parametrize("name,cols", [("C4s", 2050), ("C4s:fp8", 2050), ("C2s", 4100)])
 def test_wide_block_table(name, cols):
-    # a block table wider than the matrix-core prefill indexes (2048 columns)
-    # sends prefill to the row-wise kernel; the added columns are never named
-    # by a row's top-k ids and hold block 0
+    # a block table wider than one block window of the matrix-core prefill
+    # (2048 columns at 8 or 16 query heads per kv head); the added columns
+    # are never named by a row's top-k ids and hold block 0
     name, _, dt = name.partition(":")
     wl = make_workload(name, seed=61, **({"kv_dtype": dt} if dt else {}))
     cache = make_kv_cache(wl, DEV)
@@ -302,7 +308,7 @@ def _sweep_cases(n=24, seed=2024):
         dt = ["bf16", "fp8", "nvfp4"][int(rng.integers(3))]
         D = 128 if dt == "nvfp4" else int(rng.choice([64, 128, 128]))
         Hkv = int(rng.choice([1, 2, 4]))
-        G = int(rng.choice([1, 2, 4, 8, 8, 16, 16]))   # 8 and 16 take the matrix-core prefill
+        G = int(rng.choice([1, 2, 3, 4, 8, 8, 16, 16]))   # 3 takes the row-wise prefill
         k = int(rng.choice([1, 2, 5, 16, 33]))
         stride = int(rng.choice([8, 16]))
         rows128 = dt != "nvfp4" and stride == 8 and rng.random() < 0.3
@@ -531,8 +537,12 @@ def test_empty_context_rows_are_zero():
     # 1e-2 bound could not see a dropped block; rounding leaves ~1e-4.
     ("C2s", dict(seq_lens=[131072 + 77, 90000], k=1024, Hq=16, Hkv=2, dql=2, seed=81), 1e-3),
     ("C4s", dict(qlens=[40, 3], context=[131000, 5000], k=1024, Hq=16, Hkv=2, pad_rows=2, seed=82), 1e-3),
-    # a block table wider than the matrix-core kernel's 2048 columns (row-wise prefill)
+    # contexts spanning several block windows of the matrix-core prefill
+    # (2048 blocks at 8 query heads per kv head, 2048 at 4, 1024 at 2, 512 at 1)
     ("C4s", dict(qlens=[9, 30], context=[270000, 100], k=16, Hq=16, Hkv=2, pad_rows=1, seed=83), None),
+    ("C4s", dict(qlens=[20, 7], context=[70000, 900], k=64, Hq=8, Hkv=2, kv_dtype="fp8", seed=84), None),
+    ("C4s", dict(qlens=[33, 5], context=[40000, 300], k=64, Hq=4, Hkv=2, seed=85), None),
+    ("C4s", dict(qlens=[40, 2], context=[20000, 20], k=64, Hq=2, Hkv=2, kv_dtype="nvfp4", seed=86), None),
 ])
 def test_largest_contexts(name, kw, strict):
     _, err = _parity(make_workload(name, **kw))
