@@ -30,6 +30,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -56,6 +57,7 @@ DESCR = {
 def workload_key(args):
     """Config name, with the page format when --kv-dtype overrides it."""
     return (args.config + (f"/{args.kv_dtype}" if args.kv_dtype else "")
+            + (f"/heads{args.heads.replace('/', '-')}" if getattr(args, "heads", None) else "")
             + ("/rows128" if args.layout == "rows128" else "")
             + ("/per-block-selection" if args.selection == "per_block" else ""))
 
@@ -64,6 +66,9 @@ def describe(args):
     d = DESCR[args.config]
     if args.kv_dtype:
         d = d.replace("bf16", args.kv_dtype).replace("fp8 e4m3", args.kv_dtype).replace("NVFP4", args.kv_dtype)
+    if getattr(args, "heads", None):
+        hq, hkv = args.heads.split("/")
+        d = re.sub(r"\d+ q / \d+ kv heads", f"{hq} q / {hkv} kv heads", d)
     if args.layout == "rows128":
         d += ", 128-token pages with K|V-interleaved rows"
     if args.selection == "per_block":
@@ -293,6 +298,8 @@ def main():
                     help="top-k draws: one per row (the named workloads) or one per request and 128-token block")
     ap.add_argument("--layout", choices=["page16", "rows128"], default="page16",
                     help="cache layout (rows128: bf16 / fp8 only)")
+    ap.add_argument("--heads", default=None, metavar="Q/KV",
+                    help="query / kv head counts instead of the workload's own (e.g. 32/8)")
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -319,7 +326,7 @@ def main():
         return
     if args.also is None:
         default_main = args.config == "C2" and not args.kv_dtype and args.layout == "page16" \
-            and args.selection == "independent"
+            and args.selection == "independent" and not args.heads
         args.also = "C3,C4,C5" if default_main else ""
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -357,6 +364,7 @@ def main():
         cfg, _, kvd = name.partition("/")
         sub = argparse.Namespace(**vars(args))
         sub.config, sub.kv_dtype, sub.layout, sub.selection = cfg, (kvd or None), "page16", "independent"
+        sub.heads = None
         res = measure(sub, torch, msa, dev, keep_inputs=False)
         res.pop("_inputs", None)
         also.append({"workload": res["config"]["workload"], "value": res["value"], "unit": res["unit"],
@@ -381,8 +389,11 @@ def measure(args, torch, msa, dev, keep_inputs):
     import numpy as np
     from synth import make_kv_cache, make_query, make_workload, rows128_cache
 
-    wl = make_workload(args.config, selection=args.selection,
-                       **({"kv_dtype": args.kv_dtype} if args.kv_dtype else {}))
+    over = {"kv_dtype": args.kv_dtype} if args.kv_dtype else {}
+    if getattr(args, "heads", None):
+        hq, hkv = (int(x) for x in args.heads.split("/"))
+        over.update(Hq=hq, Hkv=hkv)
+    wl = make_workload(args.config, selection=args.selection, **over)
     print(f"[bench] {workload_key(args)}: building inputs", file=sys.stderr, flush=True)
     cache = make_kv_cache(wl, dev)
     if args.layout == "rows128":
