@@ -97,13 +97,6 @@ struct ChunkRaw<kFmtNvfp4, D> {
   uint32_t vs[2];          // page t: byte i = the scale of group r/2 of token 4g + i
 };
 
-template <class T>
-__device__ __forceinline__ T load_or_zero(bool ok, const void* p) {
-  T z;
-  __builtin_memset(&z, 0, sizeof(T));
-  return ok ? *reinterpret_cast<const T*>(p) : z;
-}
-
 // Raw-buffer descriptors (gfx9 layout, unit stride, no swizzle): a load at
 // or past num_records bytes returns 0 and touches no memory, which masks the
 // tokens past the context and blocks outside the cache without branches.
@@ -466,6 +459,23 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   } else {
     prefill_row_position(a.cu_seqlens_q, a.seq_lens, a.num_reqs, row, &req, &abs_pos);
   }
+  // Q operand rows (head kvh*G + r; padded heads r >= G read head kvh*G
+  // and drop it, so no load is lane-masked).  bf16 and fp8 pages load them,
+  // and k_scale, before the row's compaction, which their latency then
+  // overlaps, so that the waits for them cover no chunk load (measured up
+  // to 3 % faster at C3, level at C2).  NVFP4 loads them after its first
+  // chunks: loading them early measured 2 % slower at C5.
+  const int G = a.group;
+  constexpr bool kEarlyQ = FMT != kFmtNvfp4;
+  const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
+                        ((int64_t)row * a.num_q_heads + kvh * G + (r < G ? r : 0)) * D * 2;
+  u32x4 qraw[KK];
+  float kscale = 1.f;
+  if constexpr (kEarlyQ) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const u32x4*>(qrow + 2 * kappa<FMT, D>(kk, g));
+    kscale = a.k_scale ? *a.k_scale : 1.f;
+  }
   if (wave == 0) {
     const RowSlots rs = compact_row(a.topk + (int64_t)row * a.topk_stride, a.topk_k,
                                     a.block_table + (int64_t)req * a.bt_stride, a.bt_cols, abs_pos, sm.slot_list);
@@ -485,24 +495,23 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
 #pragma unroll
   for (int b = 0; b < NB; ++b)
     issue_loads<FMT, D, AUX>(raw[b], chunk_loc<FMT, D>(a, sm.slot_list, cw + nw * b, c1, ctx, kvh), lo);
+  asm volatile("" ::: "memory");
 
-  // Q operand: head kvh*G + r (zero for padded heads r >= G)
-  const int G = a.group;
-  OT qop[KK];
-  {
-    const bool ok = r < G;
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                          ((int64_t)row * a.num_q_heads + kvh * G + (ok ? r : 0)) * D * 2;
+
+  if constexpr (!kEarlyQ) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 w = load_or_zero<u32x4>(ok, qrow + 2 * kappa<FMT, D>(kk, g));
-      if constexpr (FMT == kFmtNvfp4) {
-        w = u32x4{bf16x2_to_f16x2(w[0]), bf16x2_to_f16x2(w[1]), bf16x2_to_f16x2(w[2]), bf16x2_to_f16x2(w[3])};
-      }
-      qop[kk] = __builtin_bit_cast(OT, w);
-    }
+    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const u32x4*>(qrow + 2 * kappa<FMT, D>(kk, g));
+    kscale = a.k_scale ? *a.k_scale : 1.f;
   }
-  const float kscale = a.k_scale ? *a.k_scale : 1.f;
+  OT qop[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 w = r < G ? qraw[kk] : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (FMT == kFmtNvfp4) {
+      w = u32x4{bf16x2_to_f16x2(w[0]), bf16x2_to_f16x2(w[1]), bf16x2_to_f16x2(w[2]), bf16x2_to_f16x2(w[3])};
+    }
+    qop[kk] = __builtin_bit_cast(OT, w);
+  }
   const float sl2 = a.softmax_scale * kscale * kLog2e;
 
   WaveState<FMT, D> st;
@@ -524,6 +533,9 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
         compute_chunk<FMT, D>(st, raw[b], qop, sl2, masked, c * 32 + 4 * g, L.ok ? ctx : 0);
       }
       issue_loads<FMT, D, AUX>(raw[b], chunk_loc<FMT, D>(a, sm.slot_list, c + nw * NB, c1, ctx, kvh), lo);
+      // keep these loads here, NB chunks ahead of their use: the compiler
+      // may not sink them towards the chunk that reads them
+      asm volatile("" ::: "memory");
     }
   }
 

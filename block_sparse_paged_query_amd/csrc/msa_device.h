@@ -93,6 +93,9 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // format): a load at or past num_records bytes returns 0 and touches no memory.
 constexpr int kRawBufferWord3 = 0x00020000;
 
+// A byte pointer into LDS (direct-to-LDS copies take one).
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
 // ---------------------------------------------------------------------------
 // NVFP4 slot byte order, head_dim 128 ([NV4] customize_spec leaves the bytes
 // inside a page to the kernels).  A slot holds 16 tokens: 1024 code bytes

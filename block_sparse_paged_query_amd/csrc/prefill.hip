@@ -84,7 +84,6 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 template <int D>
 __device__ __forceinline__ int k_swz(int key) { return key & (D / 8 - 1); }
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // V layout: 16-byte slot ((lc / 2) * 128 + key) * 2 + lc % 2 holds chunk lc
