@@ -695,6 +695,8 @@ hipError_t launch_gather_dequant_decode(const AttendArgs& a, int fmt, const int3
                                         const int32_t* sctx, int bps, int rows, int width_tokens, float* k_out,
                                         float* v_out, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)rows * a.num_kv_heads)), block(64);
+  log_launch("gather_dequant_decode_kernel head_dim %d: %d rows x %d kv heads, %d tokens per row", a.head_dim, rows,
+             a.num_kv_heads, width_tokens);
   if (a.head_dim == 128) {
     if (fmt == kFmtBf16)
       hipLaunchKernelGGL((gather_dequant_decode_kernel<kFmtBf16, 128>), grid, block, 0, stream, a, sbt, sbt_stride,
@@ -743,6 +745,10 @@ static hipError_t launch_fmt(const AttendArgs& a, int rows, hipStream_t stream) 
   // workgroup: stream it past the caches.  Several rows of a request (a
   // multi-token decode, prefill rows) select overlapping blocks, which the
   // L2 then serves to the neighbouring rows.
+  log_launch("attend_rows_kernel %s, %s pages, head_dim %d: %lld workgroups (row x kv head x split) of %d waves, "
+             "%d split%s, %s loads", MODE == kModeDecode ? "decode" : "prefill rows",
+             FMT == kFmtBf16 ? "bf16" : (FMT == kFmtFp8 ? "fp8" : "nvfp4"), D, (long long)blocks, nw, a.nsplit,
+             a.nsplit == 1 ? "" : "s", MODE == kModeDecode && a.dql == 1 ? "streaming" : "cached");
   bool streamed = false;
   if constexpr (MODE == kModeDecode) {
     if (a.dql == 1) {
@@ -758,6 +764,7 @@ static hipError_t launch_fmt(const AttendArgs& a, int rows, hipStream_t stream) 
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int pairs = rows * a.num_q_heads;
   const int per_block = 256 / (D / 4);
+  log_launch("attend_merge_kernel head_dim %d: %d (row, head) pairs, %d splits", D, pairs, a.nsplit);
   hipLaunchKernelGGL((attend_merge_kernel<D>), dim3((unsigned)((pairs + per_block - 1) / per_block)), dim3(256), 0,
                      stream, a, pairs);
   return hipGetLastError();

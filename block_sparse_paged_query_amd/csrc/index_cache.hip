@@ -30,6 +30,7 @@ hipError_t launch_index_insert(const void* k, int64_t ks0, int64_t ks1, int n, i
   const int64_t cap = (int64_t)num_blocks * block_size;
   int64_t blocks64 = (total + 255) / 256;
   const unsigned blocks = (unsigned)(blocks64 > 65536 ? 65536 : blocks64);
+  log_launch("index_insert_kernel: %d keys of %d x %d bytes, %u workgroups", n, d, esize, blocks);
   switch (esize) {
     case 1:
       hipLaunchKernelGGL(index_insert_kernel<uint8_t>, dim3(blocks), dim3(256), 0, stream, (const uint8_t*)k, ks0,

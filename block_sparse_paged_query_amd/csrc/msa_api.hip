@@ -3,6 +3,7 @@
 // contract of every entry point are in include/msa.h.
 #include <stdio.h>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -10,6 +11,21 @@
 #include "../../include/msa.h"
 #include "msa_device.h"
 #include "msa_internal.h"
+
+namespace msa {
+
+void log_launch(const char* fmt, ...) {
+  const char* v = getenv("MSA_LOG");
+  if (v == nullptr || v[0] == 0 || strcmp(v, "0") == 0) return;
+  char line[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof(line), fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[msa] %s\n", line);
+}
+
+}  // namespace msa
 
 namespace {
 

@@ -8,6 +8,11 @@ namespace msa {
 
 enum RowMode : int { kModeDecode = 0, kModePrefill = 1 };
 
+// Launch log: while the environment variable MSA_LOG is set to a value other
+// than "0" (read at each launch), every kernel launch writes one line to
+// stderr with the kernel and its launch shape.
+void log_launch(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
 // Arguments of the row-wise attend (decode rows, or prefill rows one by one).
 struct AttendArgs {
   const void* q;

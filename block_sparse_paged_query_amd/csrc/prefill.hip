@@ -821,6 +821,8 @@ hipError_t launch_gather_dequant_prefill(const AttendArgs& a, int fmt, const int
                                          const int32_t* sctx, int bps, int rows, int width_tokens, float* k_out,
                                          float* v_out, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)rows * a.num_kv_heads * (width_tokens / kBlockTokens))), block(kPfThreads);
+  log_launch("gather_dequant_prefill_kernel head_dim %d: %d rows x %d kv heads x %d blocks", a.head_dim, rows,
+             a.num_kv_heads, width_tokens / kBlockTokens);
   if (fmt == kFmtBf16)
     hipLaunchKernelGGL(gather_dequant_prefill_kernel<kFmtBf16>, grid, block, 0, stream, a, sbt, sbt_stride, sctx, bps,
                        width_tokens, k_out, v_out);
@@ -851,6 +853,9 @@ hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t strea
   // first request, after the last) is at most ceil(total / QT) + R + 2
   const int n_slots = (a.total_rows + QT - 1) / QT + a.num_reqs + 2;
   const dim3 grid((unsigned)((int64_t)n_slots * a.num_kv_heads));
+  log_launch("prefill_blocks_kernel %s pages, head_dim %d, %d query heads per kv head: %d tiles of %d rows x %d kv "
+             "heads, 8 waves each", fmt == kFmtBf16 ? "bf16" : (fmt == kFmtFp8 ? "fp8" : "nvfp4"), a.head_dim,
+             a.group, n_slots, QT, a.num_kv_heads);
   if (a.head_dim == 128) {
     if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 128>(a, grid, n_slots, stream);
     if (fmt == kFmtFp8) return launch_pf<kFmtFp8, 128>(a, grid, n_slots, stream);

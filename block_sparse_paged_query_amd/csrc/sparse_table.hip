@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void sparse_table_kernel(const TableArgs a) {
 
 hipError_t launch_sparse_table(const TableArgs& a, hipStream_t stream) {
   const int blocks = (a.total_q + 3) / 4;
+  log_launch("sparse_table_kernel: %d rows, top-k %d, %d workgroups of 4 waves", a.total_q, a.topk_k, blocks);
   hipLaunchKernelGGL(sparse_table_kernel, dim3(blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -87,6 +88,7 @@ __global__ __launch_bounds__(256) void query_positions_kernel(const int32_t* __r
 
 hipError_t launch_query_positions(const int32_t* cu, const int32_t* context_lens, int num_reqs, int total_q,
                                   int32_t* req_id, int32_t* abs_pos, hipStream_t stream) {
+  log_launch("query_positions_kernel: %d rows, %d requests", total_q, num_reqs);
   hipLaunchKernelGGL(query_positions_kernel, dim3((total_q + 255) / 256), dim3(256), 0, stream, cu, context_lens,
                      num_reqs, total_q, req_id, abs_pos);
   return hipGetLastError();

@@ -30,6 +30,13 @@
  *  - Rows of a top-k table must hold distinct non-negative ids (-1 pads).
  *    Repeated ids are outside the contract (the printed routine counts them
  *    twice); the library stays in bounds but the result is unspecified.
+ *  - Block-table entries naming pages outside the cache (negative, or past
+ *    num_pages) are skipped by every kernel: such a block adds nothing.
+ *  - Launch log: while the environment variable MSA_LOG is set to a value
+ *    other than "0" (read at each launch), every kernel launch writes one
+ *    line to stderr, "[msa] <kernel> ...", with its launch shape (workgroups,
+ *    waves, splits, query tile).  Validation failures are not logged; they
+ *    are reported through msa_last_error().
  */
 #ifndef MSA_H_
 #define MSA_H_

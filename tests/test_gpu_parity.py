@@ -616,3 +616,22 @@ def test_prefill_rows_before_first_request(kw):
         gen_row_pos=np.concatenate([np.full(lead, -1, np.int64), wl.gen_row_pos]))
     out, _ = _parity(shifted, cache=cache)
     assert (out[:lead].float() == 0).all()
+
+
+def test_launch_log(capfd, monkeypatch):
+    # MSA_LOG=1 prints one line per kernel launch with its shape; unset, nothing
+    dec, pre = make_workload("C2s"), make_workload("C4s", Hq=32, Hkv=8)
+    runs = [(wl, make_kv_cache(wl, DEV), make_query(wl, DEV)) for wl in (dec, pre)]
+    capfd.readouterr()
+    monkeypatch.setenv("MSA_LOG", "1")
+    for wl, cache, q in runs:
+        _run(wl, cache, q)
+    err = capfd.readouterr().err
+    # C2s: 3 rows x 8 kv heads, split so that the machine fills, then merged
+    assert "[msa] attend_rows_kernel decode, bf16 pages, head_dim 128:" in err, err
+    assert "[msa] attend_merge_kernel head_dim 128: 192 (row, head) pairs" in err, err
+    assert "[msa] prefill_blocks_kernel bf16 pages, head_dim 128, 4 query heads per kv head" in err, err
+    monkeypatch.setenv("MSA_LOG", "0")
+    for wl, cache, q in runs:
+        _run(wl, cache, q)
+    assert "[msa]" not in capfd.readouterr().err
