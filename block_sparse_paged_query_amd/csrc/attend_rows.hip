@@ -1,5 +1,5 @@
-// Row-wise block-sparse attend over a paged KV cache (decode, and prefill
-// rows taken one at a time).
+// Block-sparse decode attend over a paged KV cache: one query row (of a
+// request's decode_query_len rows) per workgroup and kv head.
 //
 // [FI] vllm.models.minimax_m3.nvidia.sparse_attention_flashinfer,
 //      MiniMaxM3SparseFlashInferImpl.forward: GQA decode over the selected
@@ -439,7 +439,7 @@ struct AttendSmem {
   float o[4][16][D];
 };
 
-template <int FMT, int D, int MODE, int AUX>
+template <int FMT, int D, int AUX>
 __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(const AttendArgs a) {
   constexpr int KK = D / 32, NN = D / 16, NB = kStages<FMT>;
   typedef typename OpType<FMT>::type OT;
@@ -454,11 +454,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   const int row = bid / a.num_kv_heads;
 
   int req, abs_pos;
-  if constexpr (MODE == kModeDecode) {
-    decode_row_position(a.seq_lens, a.dql, row, &req, &abs_pos);
-  } else {
-    prefill_row_position(a.cu_seqlens_q, a.seq_lens, a.num_reqs, row, &req, &abs_pos);
-  }
+  decode_row_position(a.seq_lens, a.dql, row, &req, &abs_pos);
   // Q operand rows (head kvh*G + r; padded heads r >= G read head kvh*G
   // and drop it, so no load is lane-masked).  bf16 and fp8 pages load them,
   // and k_scale, before the row's compaction, which their latency then
@@ -737,29 +733,22 @@ static int choose_waves(int64_t units, int waves_per_simd, int cus) {
   return best;
 }
 
-template <int FMT, int D, int MODE>
+template <int FMT, int D>
 static hipError_t launch_fmt(const AttendArgs& a, int rows, hipStream_t stream) {
   const int64_t blocks = (int64_t)rows * a.num_kv_heads * a.nsplit;
   const int nw = choose_waves(blocks, kWavesPerSimd<FMT>, a.num_cus);
   // With one query row per request each page is read by exactly one
   // workgroup: stream it past the caches.  Several rows of a request (a
-  // multi-token decode, prefill rows) select overlapping blocks, which the
-  // L2 then serves to the neighbouring rows.
-  log_launch("attend_rows_kernel %s, %s pages, head_dim %d: %lld workgroups (row x kv head x split) of %d waves, "
-             "%d split%s, %s loads", MODE == kModeDecode ? "decode" : "prefill rows",
-             FMT == kFmtBf16 ? "bf16" : (FMT == kFmtFp8 ? "fp8" : "nvfp4"), D, (long long)blocks, nw, a.nsplit,
-             a.nsplit == 1 ? "" : "s", MODE == kModeDecode && a.dql == 1 ? "streaming" : "cached");
-  bool streamed = false;
-  if constexpr (MODE == kModeDecode) {
-    if (a.dql == 1) {
-      hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE, kStreamLoads>), dim3((unsigned)blocks), dim3(64 * nw), 0,
-                         stream, a);
-      streamed = true;
-    }
-  }
-  if (!streamed) {
-    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, MODE, 0>), dim3((unsigned)blocks), dim3(64 * nw), 0, stream, a);
-  }
+  // multi-token decode) select overlapping blocks, which the L2 then serves
+  // to the neighbouring rows.
+  const bool streamed = a.dql == 1;
+  log_launch("attend_rows_kernel decode, %s pages, head_dim %d: %lld workgroups (row x kv head x split) of %d waves, "
+             "%d split%s, %s loads", FMT == kFmtBf16 ? "bf16" : (FMT == kFmtFp8 ? "fp8" : "nvfp4"), D,
+             (long long)blocks, nw, a.nsplit, a.nsplit == 1 ? "" : "s", streamed ? "streaming" : "cached");
+  if (streamed)
+    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, kStreamLoads>), dim3((unsigned)blocks), dim3(64 * nw), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, 0>), dim3((unsigned)blocks), dim3(64 * nw), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int pairs = rows * a.num_q_heads;
@@ -770,20 +759,14 @@ static hipError_t launch_fmt(const AttendArgs& a, int rows, hipStream_t stream) 
   return hipGetLastError();
 }
 
-template <int MODE>
-static hipError_t launch_mode(const AttendArgs& a, int fmt, int rows, hipStream_t stream) {
+hipError_t launch_attend_decode(const AttendArgs& a, int fmt, int rows, hipStream_t stream) {
   if (a.head_dim == 128) {
-    if (fmt == kFmtBf16) return launch_fmt<kFmtBf16, 128, MODE>(a, rows, stream);
-    if (fmt == kFmtFp8) return launch_fmt<kFmtFp8, 128, MODE>(a, rows, stream);
-    return launch_fmt<kFmtNvfp4, 128, MODE>(a, rows, stream);
+    if (fmt == kFmtBf16) return launch_fmt<kFmtBf16, 128>(a, rows, stream);
+    if (fmt == kFmtFp8) return launch_fmt<kFmtFp8, 128>(a, rows, stream);
+    return launch_fmt<kFmtNvfp4, 128>(a, rows, stream);
   }
-  if (fmt == kFmtBf16) return launch_fmt<kFmtBf16, 64, MODE>(a, rows, stream);
-  return launch_fmt<kFmtFp8, 64, MODE>(a, rows, stream);
-}
-
-hipError_t launch_attend_rows(const AttendArgs& a, int fmt, int mode, int rows, hipStream_t stream) {
-  if (mode == kModeDecode) return launch_mode<kModeDecode>(a, fmt, rows, stream);
-  return launch_mode<kModePrefill>(a, fmt, rows, stream);
+  if (fmt == kFmtBf16) return launch_fmt<kFmtBf16, 64>(a, rows, stream);
+  return launch_fmt<kFmtFp8, 64>(a, rows, stream);
 }
 
 }  // namespace msa

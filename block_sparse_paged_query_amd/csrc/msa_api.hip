@@ -363,7 +363,7 @@ static msa_status_t decode_impl(bool launch, const void* q, int32_t q_dtype, int
     a.ws_o = reinterpret_cast<float*>(base);
     a.ws_ml = a.ws_o + (size_t)rows * num_q_heads * ns * kv->head_dim;
   }
-  return hip_status(msa::launch_attend_rows(a, fmt_of(kv->kv_dtype), msa::kModeDecode, rows, stream),
+  return hip_status(msa::launch_attend_decode(a, fmt_of(kv->kv_dtype), rows, stream),
                     "decode launch");
 }
 
@@ -474,10 +474,7 @@ static msa_status_t prefill_impl(bool launch, const void* q, int32_t q_dtype, in
   a.num_reqs = num_reqs;
   a.dql = 1;
   a.total_rows = total_q;
-  if (msa::prefill_blocks_supported(a.group, kv->head_dim, fmt_of(kv->kv_dtype)))
-    return hip_status(msa::launch_prefill_blocks(a, fmt_of(kv->kv_dtype), stream), "prefill launch");
-  return hip_status(msa::launch_attend_rows(a, fmt_of(kv->kv_dtype), msa::kModePrefill, total_q, stream),
-                    "prefill launch");
+  return hip_status(msa::launch_prefill_blocks(a, fmt_of(kv->kv_dtype), stream), "prefill launch");
 }
 
 MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,
@@ -564,8 +561,8 @@ MSA_API msa_status_t msa_debug_gather_dequant(const msa_kv_cache_t* kv, const in
   MSA_CHECK(kv->num_kv_heads >= 1, MSA_ERR_INVALID_ARGUMENT, "num_kv_heads %d < 1", kv->num_kv_heads);
   MSA_CHECK(path == 0 || path == 1, MSA_ERR_INVALID_ARGUMENT, "path %d: 0 (decode gather) or 1 (prefill staging)",
             path);
-  MSA_CHECK(kv->head_dim == 128 || (kv->head_dim == 64 && path == 0 && kv->kv_dtype != MSA_NVFP4),
-            MSA_ERR_UNSUPPORTED, "head_dim %d: 128, or 64 for bf16 / fp8 pages on the decode path", kv->head_dim);
+  MSA_CHECK(kv->head_dim == 128 || (kv->head_dim == 64 && kv->kv_dtype != MSA_NVFP4), MSA_ERR_UNSUPPORTED,
+            "head_dim %d: 128, or 64 for bf16 / fp8 pages", kv->head_dim);
   {
     const msa_status_t st = check_kv_geometry(kv);
     if (st != MSA_OK) return st;

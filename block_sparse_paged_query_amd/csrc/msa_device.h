@@ -177,24 +177,4 @@ __device__ __forceinline__ void decode_row_position(const int32_t* __restrict__ 
   *abs_pos = seq_lens[r] - dql + (row - r * dql);
 }
 
-// Row position in prefill: the request whose [cu[r], cu[r+1]) holds the row,
-// at seq_lens[r] - (cu[r+1] - cu[r]) + (row - cu[r]); rows past cu[R] are
-// padding (position -1).
-__device__ __forceinline__ void prefill_row_position(const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_lens,
-                                                     int num_reqs, int row, int* req, int* abs_pos) {
-  int lo = 0, hi = num_reqs;  // find the last r with cu[r] <= row
-  if (row >= cu[num_reqs] || row < cu[0]) {
-    *req = 0;
-    *abs_pos = -1;
-    return;
-  }
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= row) lo = mid; else hi = mid;
-  }
-  const int start = cu[lo], end = cu[lo + 1];
-  *req = lo;
-  *abs_pos = seq_lens[lo] - (end - start) + (row - start);
-}
-
 }  // namespace msa

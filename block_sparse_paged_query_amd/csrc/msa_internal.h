@@ -6,14 +6,12 @@
 
 namespace msa {
 
-enum RowMode : int { kModeDecode = 0, kModePrefill = 1 };
-
 // Launch log: while the environment variable MSA_LOG is set to a value other
 // than "0" (read at each launch), every kernel launch writes one line to
 // stderr with the kernel and its launch shape.
 void log_launch(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 
-// Arguments of the row-wise attend (decode rows, or prefill rows one by one).
+// Arguments of the attends (decode rows, prefill query tiles).
 struct AttendArgs {
   const void* q;
   void* out;
@@ -58,12 +56,11 @@ struct AttendArgs {
   int32_t num_cus;   // compute units of the device (launch shaping)
 };
 
-hipError_t launch_attend_rows(const AttendArgs& a, int fmt, int mode, int rows, hipStream_t stream);
+hipError_t launch_attend_decode(const AttendArgs& a, int fmt, int rows, hipStream_t stream);
 
 // Matrix-core prefill over query tiles: bf16, fp8 or NVFP4 pages; head_dim
-// 128 (or 64 for bf16 and fp8); 1, 2, 4, 8 or 16 query heads per kv head.
-// Other head groups take the row-wise kernel.
-bool prefill_blocks_supported(int group, int head_dim, int fmt);
+// 128 (or 64 for bf16 and fp8); 1 to 16 query heads per kv head (every shape
+// the C ABI accepts).
 hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t stream);
 
 struct TableArgs {

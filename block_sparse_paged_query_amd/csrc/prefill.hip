@@ -10,8 +10,9 @@
 //      _write_sparse_block_table_row_from_values (the tokens a row sees).
 //
 // Work decomposition.  A workgroup (8 waves) owns one kv head and QT
-// consecutive query rows of one request (QT = 256 / G for G query heads per
-// kv head: 16 rows at G = 16, 256 at G = 1).  Every query row picks its own
+// consecutive query rows of one request (QT = 16 RT, RT = floor(16 / G) rows
+// per matrix tile for G query heads per kv head: 16 rows at G >= 9, 256 at
+// G = 1; a tile's 16 - RT G spare columns stay masked).  Every query row picks its own
 // blocks, so the workgroup first builds, per block of the request, the bit
 // mask of its rows that selected it (and may see it causally), then walks
 // the blocks some row selected in ascending order (a window of blocks at a
@@ -48,10 +49,10 @@ namespace msa {
 constexpr int kPfWaves = 8;                 // two per SIMD: one's softmax overlaps the other's MFMAs
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfTiles = 2;                 // matrix tiles per wave
-// Row masks: a workgroup tile has QT = 16 * 16 / G rows (32 for 8 query heads
-// per kv head, 256 for 1), so a block's mask is MW = QT / 32 words; the block
-// masks of a window of kPfWindow<MW> blocks are held at once (a request with
-// more blocks is walked window by window).
+// Row masks: a workgroup tile has QT = 16 RT rows (32 for 8 query heads per
+// kv head, 80 for 3, 256 for 1), so a block's mask is MW = ceil(QT / 32)
+// words; the block masks of a window of kPfWindow<MW> blocks are held at once
+// (a request with more blocks is walked window by window).
 template <int MW>
 constexpr int kPfWindow = MW <= 2 ? 2048 : 4096 / MW;
 // one block of K (or V) in the compute layout: 128 keys x D bf16 / fp16
@@ -650,8 +651,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
     }
     __syncthreads();
     const int n_act = s_info[0];
+    // (readfirstlane returns int: shift the words as unsigned, or a set top
+    // bit would smear into the bits of the next word)
     auto wave_mask = [&](int jl) -> uint32_t {
-      return (__builtin_amdgcn_readfirstlane(s_mask[jl][wword]) >> wshift) & wave_bits;
+      uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane(s_mask[jl][wword]) >> wshift;
+      if constexpr (MW > 1) {
+        // a wave's 2 RT bits run into the next word when 2 RT does not divide 32
+        if (wshift + kPfTiles * RT > 32)
+          m |= (uint32_t)__builtin_amdgcn_readfirstlane(s_mask[jl][wword + 1]) << (32 - wshift);
+      }
+      return m & wave_bits;
     };
 
     if constexpr (FMT == kFmtBf16) {
@@ -741,14 +750,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
 // k_scale / v_scale in fp32; keys at or past the row's context in the slot,
 // and blocks outside the cache, give 0.  out[row][token][kv head][d].
 // ---------------------------------------------------------------------------
-template <int FMT>
+template <int FMT, int D>
 __global__ __launch_bounds__(kPfThreads) void gather_dequant_prefill_kernel(const AttendArgs a,
                                                                             const int32_t* __restrict__ sbt,
                                                                             int64_t sbt_stride,
                                                                             const int32_t* __restrict__ sctx, int bps,
                                                                             int width_tokens, float* __restrict__ k_out,
                                                                             float* __restrict__ v_out) {
-  constexpr int D = 128;
+  constexpr int NPK = D / 16;   // 16-element pieces of a key row
   __shared__ __align__(16) uint8_t bK[FMT == kFmtBf16 ? kPfBlockBytes<D> : 16];
   __shared__ __align__(16) uint8_t bV[FMT == kFmtBf16 ? kPfBlockBytes<D> : kPfRawBytes<FMT, D>];
   const int tid = threadIdx.x;
@@ -773,19 +782,19 @@ __global__ __launch_bounds__(kPfThreads) void gather_dequant_prefill_kernel(cons
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
-  // item q: side q / 1024, key, 16-element piece n (d = 16 n .. 16 n + 15)
-  for (int q = tid; q < 2 * kBlockTokens * 8; q += kPfThreads) {
-    const bool v_side = q >= kBlockTokens * 8;
-    const int key = (q >> 3) & (kBlockTokens - 1), n = q & 7;
+  // item q: side q / (128 NPK), key, 16-element piece n (d = 16 n .. 16 n + 15)
+  for (int q = tid; q < 2 * kBlockTokens * NPK; q += kPfThreads) {
+    const bool v_side = q >= kBlockTokens * NPK;
+    const int key = (q / NPK) & (kBlockTokens - 1), n = q % NPK;
     uint32_t o[8];
     if constexpr (FMT == kFmtBf16) {
-      // K rows: 16-byte chunk c of key at chunk c ^ (key & 15); V: chunk lc of
-      // key in the 16-byte slot ((lc / 2) * 128 + key) * 2 + lc % 2
+      // K rows (2 D bytes): 16-byte chunk c of key at chunk c ^ k_swz(key);
+      // V: chunk lc of key in the 16-byte slot ((lc / 2) * 128 + key) * 2 + lc % 2
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int c = 2 * n + h;
         const uint8_t* src = v_side ? bV + (((c >> 1) * kBlockTokens + key) * 2 + (c & 1)) * 16
-                                    : bK + key * 256 + ((c ^ k_swz<D>(key)) << 4);
+                                    : bK + key * (2 * D) + ((c ^ k_swz<D>(key)) << 4);
         const u32x4 w = *reinterpret_cast<const u32x4*>(src);
         o[4 * h + 0] = w[0];
         o[4 * h + 1] = w[1];
@@ -823,25 +832,32 @@ hipError_t launch_gather_dequant_prefill(const AttendArgs& a, int fmt, const int
   const dim3 grid((unsigned)((int64_t)rows * a.num_kv_heads * (width_tokens / kBlockTokens))), block(kPfThreads);
   log_launch("gather_dequant_prefill_kernel head_dim %d: %d rows x %d kv heads x %d blocks", a.head_dim, rows,
              a.num_kv_heads, width_tokens / kBlockTokens);
-  if (fmt == kFmtBf16)
-    hipLaunchKernelGGL(gather_dequant_prefill_kernel<kFmtBf16>, grid, block, 0, stream, a, sbt, sbt_stride, sctx, bps,
-                       width_tokens, k_out, v_out);
-  else if (fmt == kFmtFp8)
-    hipLaunchKernelGGL(gather_dequant_prefill_kernel<kFmtFp8>, grid, block, 0, stream, a, sbt, sbt_stride, sctx, bps,
-                       width_tokens, k_out, v_out);
-  else
-    hipLaunchKernelGGL(gather_dequant_prefill_kernel<kFmtNvfp4>, grid, block, 0, stream, a, sbt, sbt_stride, sctx,
-                       bps, width_tokens, k_out, v_out);
+#define MSA_GATHER_PF(F, DD)                                                                                       \
+  hipLaunchKernelGGL((gather_dequant_prefill_kernel<F, DD>), grid, block, 0, stream, a, sbt, sbt_stride, sctx, bps, \
+                     width_tokens, k_out, v_out)
+  if (a.head_dim == 128) {
+    if (fmt == kFmtBf16) MSA_GATHER_PF(kFmtBf16, 128);
+    else if (fmt == kFmtFp8) MSA_GATHER_PF(kFmtFp8, 128);
+    else MSA_GATHER_PF(kFmtNvfp4, 128);
+  } else {
+    if (fmt == kFmtBf16) MSA_GATHER_PF(kFmtBf16, 64);
+    else MSA_GATHER_PF(kFmtFp8, 64);
+  }
+#undef MSA_GATHER_PF
   return hipGetLastError();
 }
 
+// Row-mask words per block: ceil(16 RT / 32) for RT = floor(16 / G) rows per
+// tile, so 8 at G = 1, 4 at 2, 3 at 3, 2 at 4 and 5, 1 from 6 up.
+static int pf_mask_words(int group) { return (16 / group + 1) / 2; }
+
 template <int FMT, int D>
 static hipError_t launch_pf(const AttendArgs& a, dim3 grid, int n_slots, hipStream_t stream) {
-  switch (a.group) {
-    case 16:
-    case 8: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 1>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
-    case 4: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 2>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
-    case 2: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 4>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
+  switch (pf_mask_words(a.group)) {
+    case 1: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 1>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
+    case 2: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 2>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
+    case 3: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 3>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
+    case 4: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 4>), grid, dim3(kPfThreads), 0, stream, a, n_slots); break;
     default: hipLaunchKernelGGL((prefill_blocks_kernel<FMT, D, 8>), grid, dim3(kPfThreads), 0, stream, a, n_slots);
   }
   return hipGetLastError();
@@ -863,13 +879,6 @@ hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t strea
   }
   if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 64>(a, grid, n_slots, stream);
   return launch_pf<kFmtFp8, 64>(a, grid, n_slots, stream);
-}
-
-// Query groups that divide a 16-column tile into whole rows; head_dim 64 or
-// 128 (NVFP4: 128); any block-table width (windows of blocks).
-bool prefill_blocks_supported(int group, int head_dim, int fmt) {
-  const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
-  return g_ok && (head_dim == 128 || (head_dim == 64 && fmt != kFmtNvfp4));
 }
 
 }  // namespace msa

@@ -340,7 +340,7 @@ MSA_API msa_status_t msa_insert_index_cache(
  * path 0: the decode attend's gather (chunk addressing, page loads masked at
  *   the context, in-register conversion to the operand types);
  * path 1: the prefill attend's staging (the block copied into LDS, fp8 /
- *   NVFP4 converted there; head_dim 128).
+ *   NVFP4 converted there).
  * k_out, v_out [total_q][16 * sbt_width][num_kv_heads][head_dim] fp32: the
  * operand element (bf16 / fp8 / e2m1 x E4M3 block scale, exact in the
  * operand type) times k_scale or v_scale, rounded to nearest fp32.  Tokens at

@@ -148,7 +148,8 @@ C4S_ROWS = [0, 1, 127, 128, 299, 300, 301, 555, 700, 816, 817, 818, 821]
 
 
 @pytest.mark.parametrize("name,kw", [("C4s", dict(kv_dtype="fp8")), ("C4s", dict(kv_dtype="nvfp4")),
-                                     ("C3s", dict(block_page_stride=16))])
+                                     ("C3s", dict(block_page_stride=16)), ("C4s", dict(D=64, Hq=16, Hkv=2)),
+                                     ("C4s", dict(D=64, Hq=16, Hkv=2, kv_dtype="fp8"))])
 def test_gather_dequant_bit_exact_variants(name, kw):
     wl = make_workload(name, **kw)
     _hook_vs_oracle(wl, make_kv_cache(wl, DEV), rows=C4S_ROWS if name == "C4s" else None)
@@ -232,8 +233,16 @@ def test_prefill_parity_small():
     dict(Hq=4, Hkv=4, seed=57),                          # 1 per kv head: eight mask words
     dict(Hq=8, Hkv=4, seed=58),                          # 2 per kv head: four mask words
     dict(D=64, Hq=8, Hkv=8, kv_dtype="fp8", seed=59),    # head_dim 64, fp8 pages, 1 per kv head
-    dict(Hq=12, Hkv=4, seed=60),                         # 3 per kv head: row-wise kernel
-    dict(Hq=12, Hkv=2, kv_dtype="nvfp4", seed=62),       # 6 per kv head: row-wise kernel
+    dict(Hq=12, Hkv=4, seed=60),                         # 3 per kv head: 5-row tiles, three mask words
+    dict(Hq=12, Hkv=2, kv_dtype="nvfp4", seed=62),       # 6 per kv head: 2-row tiles, 4 spare columns
+    dict(Hq=10, Hkv=2, seed=64),                         # 5 per kv head: wave masks straddle words
+    # sparse selections (top-k 2 of ~22 blocks), so rows whose mask bits
+    # straddle a word pick other blocks than their neighbours: 5 and 3 per kv head
+    dict(Hq=10, Hkv=2, k=2, qlens=[25, 67], context=[2090, 2791], pad_rows=3, seed=68),
+    dict(Hq=6, Hkv=2, k=2, qlens=[25, 67], context=[2090, 2791], pad_rows=3, seed=69),
+    dict(Hq=7, Hkv=1, kv_dtype="fp8", seed=65),          # 7 per kv head
+    dict(D=64, Hq=12, Hkv=1, seed=66),                   # 12 per kv head: 1-row tiles, head_dim 64
+    dict(Hq=15, Hkv=1, kv_dtype="nvfp4", seed=67),       # 15 per kv head
     dict(block_page_stride=16, seed=44),                 # K and V sides in one block
     dict(qlens=[1, 40, 700], context=[3000, 0, 129], seed=45),   # long context, tiny request
     dict(qlens=[0, 300], context=[50, 0], seed=46),      # an empty request
@@ -308,7 +317,7 @@ def _sweep_cases(n=24, seed=2024):
         dt = ["bf16", "fp8", "nvfp4"][int(rng.integers(3))]
         D = 128 if dt == "nvfp4" else int(rng.choice([64, 128, 128]))
         Hkv = int(rng.choice([1, 2, 4]))
-        G = int(rng.choice([1, 2, 3, 4, 8, 8, 16, 16]))   # 3 takes the row-wise prefill
+        G = int(rng.choice([1, 2, 3, 4, 8, 8, 16, 16]))
         k = int(rng.choice([1, 2, 5, 16, 33]))
         stride = int(rng.choice([8, 16]))
         rows128 = dt != "nvfp4" and stride == 8 and rng.random() < 0.3
@@ -538,11 +547,14 @@ def test_empty_context_rows_are_zero():
     ("C2s", dict(seq_lens=[131072 + 77, 90000], k=1024, Hq=16, Hkv=2, dql=2, seed=81), 1e-3),
     ("C4s", dict(qlens=[40, 3], context=[131000, 5000], k=1024, Hq=16, Hkv=2, pad_rows=2, seed=82), 1e-3),
     # contexts spanning several block windows of the matrix-core prefill
-    # (2048 blocks at 8 query heads per kv head, 2048 at 4, 1024 at 2, 512 at 1)
+    # (2048 blocks at 8 query heads per kv head, 2048 at 4, 1365 at 3, 1024 at
+    # 2, 512 at 1)
     ("C4s", dict(qlens=[9, 30], context=[270000, 100], k=16, Hq=16, Hkv=2, pad_rows=1, seed=83), None),
     ("C4s", dict(qlens=[20, 7], context=[70000, 900], k=64, Hq=8, Hkv=2, kv_dtype="fp8", seed=84), None),
     ("C4s", dict(qlens=[33, 5], context=[40000, 300], k=64, Hq=4, Hkv=2, seed=85), None),
     ("C4s", dict(qlens=[40, 2], context=[20000, 20], k=64, Hq=2, Hkv=2, kv_dtype="nvfp4", seed=86), None),
+    # 3 query heads per kv head: 80-row tiles, windows of 1365 blocks
+    ("C4s", dict(qlens=[90, 4], context=[180000, 60], k=32, Hq=6, Hkv=2, seed=87), None),
 ])
 def test_largest_contexts(name, kw, strict):
     _, err = _parity(make_workload(name, **kw))
@@ -597,11 +609,11 @@ def test_index_cache_insert_bit_exact(dtype):
     assert (raw(gc.cpu()) == want).all()
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(Hq=16, Hkv=4), dict(kv_dtype="fp8")])
+@pytest.mark.parametrize("kw", [dict(), dict(Hq=16, Hkv=4), dict(kv_dtype="fp8"), dict(Hq=12, Hkv=4)])
 def test_prefill_rows_before_first_request(kw):
     # cu_seqlens_q[0] > 0: the rows before the first request are padding and
-    # come out 0, on the matrix-core kernel (8 heads per kv head) and on the
-    # row-wise kernel (4 per kv head) alike; the cache is the unshifted one
+    # come out 0, at 8, 4 and 3 query heads per kv head (query tiles of 32,
+    # 64 and 80 rows); the cache is the unshifted one
     wl = make_workload("C4s", seed=57, **kw)
     cache = make_kv_cache(wl, DEV)
     lead = 37
