@@ -55,6 +55,11 @@ constexpr int kPfTiles = 2;                 // matrix tiles per wave
 // (a request with more blocks is walked window by window).
 template <int MW>
 constexpr int kPfWindow = MW <= 2 ? 2048 : 4096 / MW;
+// NVFP4 holds two compute-layout blocks (4 x 32 KB) and one raw block
+// (18 KB): its window is what the rest of the 160 KB leaves for the tables
+// (per block: MW mask words, a list entry and a physical id).
+template <int MW>
+constexpr int kPfWindowAhead = ((160 * 1024 - 4 * 32768 - 8 * 2 * 9 * 128 - 512) / (4 * MW + 6)) & ~63;
 // one block of K (or V) in the compute layout: 128 keys x D bf16 / fp16
 template <int D>
 constexpr int kPfBlockBytes = kBlockTokens * 2 * D;
@@ -356,6 +361,8 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT, D>& w, const uint8_t
 //          writes the V layout with consecutive lanes on consecutive keys.
 //   NVFP4: the block's 8 pages, each the K slot then the V slot of kvh
 //          (2 x 1152 B, adjacent in the page), piece q at q (head_dim 128).
+//          Wave w copies page w (two full instructions and 16 lanes of a
+//          third), so the wave that converts a page has copied it itself.
 template <int FMT, int D>
 __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a, int kvh, int phys) {
   constexpr int NPK = D / 16, HALF = kBlockTokens * NPK;   // pieces per key row; K pieces
@@ -383,16 +390,13 @@ __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a,
                                                  0, 0, 0);
       }
     } else {
-      constexpr int SLOT = 9 * 128, PAGE_PIECES = 2 * SLOT / 16;   // 144 pieces of 16 B per page
+      constexpr int PAGE = 2 * kNvfp4SlotBytes, TAIL = PAGE / 16 - 128;   // 2304 B; 16 pieces past 2 KB
       const __amdgpu_buffer_rsrc_t r_ = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(a.k_base + boff), (short)0, 7 * sub + 2 * SLOT, kRawBufferWord3);
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        if (k == 2 && wave >= 2) break;   // 1152 pieces: the third pass is two waves
-        const int q = k * kPfThreads + wave * 64 + lane;
-        const int page = q / PAGE_PIECES, off = page * sub + (q - page * PAGE_PIECES) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, raw + (k * kPfThreads + wave * 64) * 16, 16, off, 0, 0, 0);
-      }
+          const_cast<uint8_t*>(a.k_base + boff + (int64_t)wave * sub), (short)0, PAGE, kRawBufferWord3);
+      lds_u8* dst = raw + wave * PAGE;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, dst, 16, 16 * lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, dst + 1024, 16, 1024 + 16 * lane, 0, 0, 0);
+      if (lane < TAIL) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, dst + 2048, 16, 2048 + 16 * lane, 0, 0, 0);
     }
     return;
   }
@@ -412,15 +416,12 @@ __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a,
       __builtin_amdgcn_global_load_lds(src, raw + (k * kPfThreads + wave * 64) * 16, 16, 0, 0);
     }
   } else {
-    constexpr int SLOT = 9 * 128, PAGE_PIECES = 2 * SLOT / 16;   // 144 pieces of 16 B per page
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      if (k == 2 && wave >= 2) break;   // 1152 pieces: the third pass is two waves
-      const int q = k * kPfThreads + wave * 64 + lane;
-      const int page = q / PAGE_PIECES, off = (q - page * PAGE_PIECES) * 16;
-      __builtin_amdgcn_global_load_lds(a.k_base + boff + page * a.sub_stride + off,
-                                       raw + (k * kPfThreads + wave * 64) * 16, 16, 0, 0);
-    }
+    constexpr int PAGE = 2 * kNvfp4SlotBytes, TAIL = PAGE / 16 - 128;
+    const uint8_t* src = a.k_base + boff + (int64_t)wave * a.sub_stride + 16 * lane;
+    lds_u8* dst = raw + wave * PAGE;
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + 1024, dst + 1024, 16, 0, 0);
+    if (lane < TAIL) __builtin_amdgcn_global_load_lds(src + 2048, dst + 2048, 16, 0, 0);
   }
 }
 
@@ -488,17 +489,55 @@ __device__ __forceinline__ void pf_stage_convert(const uint8_t* raw, uint8_t* kc
   }
 }
 
+// NVFP4, one quarter of the calling wave's own page: wave w converts the 16
+// keys of page w (the page it copied), items q = 64 part + lane of 256: K
+// items first (key 16 w + q / 8, piece q % 8), then V items (key 16 w +
+// q % 16, piece (q - 128) / 16, consecutive lanes on consecutive keys).
+template <int D>
+__device__ __forceinline__ void pf_convert_own_page(const uint8_t* raw, uint8_t* kc, uint8_t* vc, int nkeys,
+                                                    int part) {
+  static_assert(D == 128, "NVFP4 pages hold head_dim 128");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const bool v_side = part >= 2;
+  const int local = (64 * part + lane) & 127;
+  const int key = 16 * wave + (v_side ? (local & 15) : (local >> 3));
+  const int n = v_side ? (local >> 4) : (local & 7);
+  uint32_t o[8];
+  pf_stage_item<kFmtNvfp4, D>(raw, v_side, key, n, o);
+  if (key >= nkeys) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = 0u;
+  }
+  const u32x4 c0 = {o[0], o[1], o[2], o[3]}, c1 = {o[4], o[5], o[6], o[7]};
+  if (!v_side) {
+    const int sw = k_swz<D>(key);
+    *reinterpret_cast<u32x4*>(kc + key * (2 * D) + (((2 * n) ^ sw) << 4)) = c0;
+    *reinterpret_cast<u32x4*>(kc + key * (2 * D) + (((2 * n + 1) ^ sw) << 4)) = c1;
+  } else {
+    *reinterpret_cast<u32x4*>(vc + (n * 128 + key) * 32) = c0;
+    *reinterpret_cast<u32x4*>(vc + (n * 128 + key) * 32 + 16) = c1;
+  }
+}
+
 template <int FMT, int D, int MW>
 __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const AttendArgs a, int n_slots) {
   typedef typename PfOp<FMT>::type OT;
   typedef typename PfPv<FMT>::type PT;
-  constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN, WIN = kPfWindow<MW>;
+  // NVFP4 converts the next block while the current one computes (two
+  // compute-layout buffers, one raw buffer); fp8 has no room for that
+  constexpr bool kAhead = FMT == kFmtNvfp4;
+  constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN,
+                WIN = kAhead ? kPfWindowAhead<MW> : kPfWindow<MW>;
   // Four LDS buffers as distinct objects: the loops below are unrolled by two,
   // so the compiler knows the in-flight copies target another buffer.
   //   bf16:        K / V double buffers (bA, bC) and (bB, bD)
   //   fp8 / NVFP4: compute K, V (bA, bB) and raw staging buffers bC, bD
   __shared__ __align__(16) uint8_t bA[kPfBlockBytes<D>], bB[kPfBlockBytes<D>];
-  __shared__ __align__(16) uint8_t bC[kPfRawBytes<FMT, D>], bD[kPfRawBytes<FMT, D>];
+  __shared__ __align__(16) uint8_t bC[kAhead ? kPfBlockBytes<D> : kPfRawBytes<FMT, D>];
+  __shared__ __align__(16) uint8_t bD[kAhead ? kPfBlockBytes<D> : kPfRawBytes<FMT, D>];
+  __shared__ __align__(16) uint8_t bE[kAhead ? kPfRawBytes<FMT, D> : 16];
   __shared__ uint32_t s_mask[WIN][MW];        // per block of the window: its selecting rows
   __shared__ uint16_t s_list[WIN];            // selected blocks of the window, ascending
   __shared__ int32_t s_phys[WIN];             // their physical block ids
@@ -688,6 +727,45 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
                              it + 2 < n_act ? w0 + (int)s_list[it + 2] : 0, it + 2 < n_act};
           pf_compute_block<D, OT, PT>(w, bB, bD, wave_mask(jl), j, RT, sl2, j >= own_first, nx, a, kvh, seq_len);
           __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+        }
+      }
+    } else if constexpr (kAhead) {
+      // NVFP4: raw block in bE; each wave copies and converts its own page
+      // (no barrier between the two), into (bA, bB) or (bC, bD).  The step
+      // that computes block i first converts block i+1 into the other
+      // compute buffers and issues block i+2's copy: one barrier per block.
+      const PfNext none = {nullptr, nullptr, 0, 0, false};
+      auto convert = [&](int idx, uint8_t* kc, uint8_t* vc) {
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's copy of its page has landed
+        const int nk = seq_len - (w0 + (int)s_list[idx]) * kBlockTokens;
+#pragma unroll
+        for (int part = 0; part < 4; ++part) pf_convert_own_page<D>(bE, kc, vc, nk, part);
+      };
+      if (n_act > 0) {
+        pf_stage_issue<FMT, D>((lds_u8*)bE, a, kvh, s_phys[0]);
+        convert(0, bA, bB);
+        if (n_act > 1) pf_stage_issue<FMT, D>((lds_u8*)bE, a, kvh, s_phys[1]);
+      }
+      __syncthreads();
+      for (int it = 0; it < n_act; it += 2) {
+        {
+          const int jl = s_list[it], j = w0 + jl;
+          if (it + 1 < n_act) {
+            convert(it + 1, bC, bD);
+            if (it + 2 < n_act) pf_stage_issue<FMT, D>((lds_u8*)bE, a, kvh, s_phys[it + 2]);
+          }
+          pf_compute_block<D, OT, PT>(w, bA, bB, wave_mask(jl), j, RT, sl2, j >= own_first, none, a, kvh, seq_len);
+          __syncthreads();   // every wave is done with (bA, bB), and (bC, bD) holds block it + 1
+        }
+        if (it + 1 >= n_act) break;
+        {
+          const int jl = s_list[it + 1], j = w0 + jl;
+          if (it + 2 < n_act) {
+            convert(it + 2, bA, bB);
+            if (it + 3 < n_act) pf_stage_issue<FMT, D>((lds_u8*)bE, a, kvh, s_phys[it + 3]);
+          }
+          pf_compute_block<D, OT, PT>(w, bC, bD, wave_mask(jl), j, RT, sl2, j >= own_first, none, a, kvh, seq_len);
           __syncthreads();
         }
       }
