@@ -35,12 +35,15 @@
 //
 // fp8 and NVFP4 pages ([FI] forward folds the fp8 scales; [NV4] customize_spec
 // for the two NVFP4 slots) take a staged path: the selected block's raw bytes
-// (half or a quarter of bf16's) go into a double-buffered LDS staging area,
-// and at the start of each block the workgroup converts them exactly (fp8 ->
+// (half or a quarter of bf16's) go into LDS and are converted exactly (fp8 ->
 // bf16; e2m1 x E4M3 block scale -> fp16) into the same K / V layouts the
-// bf16 path reads, so the matrix-core loop is shared.  NVFP4 computes in
-// fp16 (the query is converted once), fp8 in bf16; the per-tensor scales
-// fold into the softmax scale and the output as in the decode.
+// bf16 path reads, so the matrix-core loop is shared.  fp8 stages into two
+// raw buffers and converts each block at its start; NVFP4 (a smaller raw
+// block) keeps two compute-layout buffers and converts the next block while
+// the current one computes, each wave converting the page it copied.  NVFP4
+// computes in fp16 (the query is converted once), fp8 in bf16; the
+// per-tensor scales fold into the softmax scale and the output as in the
+// decode.
 #include "msa_device.h"
 #include "msa_internal.h"
 
