@@ -548,11 +548,13 @@ def test_empty_context_rows_are_zero():
     ("C4s", dict(qlens=[40, 3], context=[131000, 5000], k=1024, Hq=16, Hkv=2, pad_rows=2, seed=82), 1e-3),
     # contexts spanning several block windows of the matrix-core prefill
     # (2048 blocks at 8 query heads per kv head, 2048 at 4, 1365 at 3, 1024 at
-    # 2, 512 at 1)
+    # 2, 512 at 1; NVFP4 1344, 960, 768, 576 and 320)
     ("C4s", dict(qlens=[9, 30], context=[270000, 100], k=16, Hq=16, Hkv=2, pad_rows=1, seed=83), None),
     ("C4s", dict(qlens=[20, 7], context=[70000, 900], k=64, Hq=8, Hkv=2, kv_dtype="fp8", seed=84), None),
     ("C4s", dict(qlens=[33, 5], context=[40000, 300], k=64, Hq=4, Hkv=2, seed=85), None),
-    ("C4s", dict(qlens=[40, 2], context=[20000, 20], k=64, Hq=2, Hkv=2, kv_dtype="nvfp4", seed=86), None),
+    ("C4s", dict(qlens=[40, 2], context=[50000, 20], k=64, Hq=2, Hkv=2, kv_dtype="nvfp4", seed=86), None),
+    # NVFP4 walks shorter windows (it keeps two compute buffers): 1344 blocks at 8 per kv head
+    ("C4s", dict(qlens=[12, 3], context=[200000, 40], k=24, Hq=16, Hkv=2, kv_dtype="nvfp4", seed=88), None),
     # 3 query heads per kv head: 80-row tiles, windows of 1365 blocks
     ("C4s", dict(qlens=[90, 4], context=[180000, 60], k=32, Hq=6, Hkv=2, seed=87), None),
 ])
