@@ -93,13 +93,13 @@ hipError_t launch_index_insert(const void* k, int64_t ks0, int64_t ks1, int n, i
 
 // Test hook: each row's K / V in sparse-table order through the decode
 // attend's gather (launch_gather_dequant_decode) or the prefill attend's
-// staged copy (launch_gather_dequant_prefill; head_dim 128).
+// staged copy (launch_gather_dequant_prefill); head_dim 128, or 64 for bf16
+// and fp8 pages.
 hipError_t launch_gather_dequant_decode(const AttendArgs& a, int fmt, const int32_t* sbt, int64_t sbt_stride,
                                         const int32_t* sctx, int bps, int rows, int width_tokens, float* k_out,
                                         float* v_out, hipStream_t stream);
 hipError_t launch_gather_dequant_prefill(const AttendArgs& a, int fmt, const int32_t* sbt, int64_t sbt_stride,
                                          const int32_t* sctx, int bps, int rows, int width_tokens, float* k_out,
                                          float* v_out, hipStream_t stream);
-
 
 }  // namespace msa
