@@ -11,16 +11,18 @@
 // [SPA] vllm.models.minimax_m3.amd.ops.sparse_pa,
 //      _write_sparse_block_table_row_from_values: which tokens a row sees.
 //
-// Work decomposition.  One workgroup (W = 3 or 4 waves, chosen at launch so
-// that the grid fills whole rounds of the machine) owns (row, kv head,
-// split).  Wave 0 compacts the row's top-k ids into the slot list (full
-// blocks, then the causal tail) in LDS.  The row's context [0, ctx) is cut
-// into 32-token chunks (two 16-token pages of one 128-token block); a split
-// owns a contiguous range of chunks and its W waves take every W-th chunk.
-// Each wave keeps its own online-softmax state and several chunks' loads in
-// flight; the W states are merged through LDS at the end.  With one split
-// the workgroup writes the bf16 output directly; otherwise it writes an fp32
-// partial (o, m, l) and attend_merge combines.
+// Work decomposition.  A unit (row, kv head, split) is served by W = 3 or 4
+// waves, chosen at launch so that the grid fills whole rounds of the
+// machine; a workgroup holds one unit, or four 3-wave units when they fill
+// the machine once (see attend_rows_kernel).  The unit's first wave compacts
+// the row's top-k ids into the slot list (full blocks, then the causal tail)
+// in LDS.  The row's context [0, ctx) is cut into 32-token chunks (two
+// 16-token pages of one 128-token block); a split owns a contiguous range of
+// chunks and its W waves take every W-th chunk.  Each wave keeps its own
+// online-softmax state and several chunks' loads in flight; the W states are
+// merged through LDS at the end.  With one split the unit writes the bf16
+// output directly; otherwise it writes an fp32 partial (o, m, l) and
+// attend_merge combines.
 //
 // Loads go through raw-buffer descriptors built per page in scalar
 // registers, sized to the page's tokens inside the context: the hardware
@@ -430,24 +432,41 @@ __device__ __forceinline__ void compute_chunk(WaveState<FMT, D>& st, const Chunk
 }
 
 // Shared memory of one workgroup.
-template <int D>
+// One unit's LDS: its slot list and the merge area of its (up to) NW waves.
+template <int D, int NW>
 struct AttendSmem {
   int slot_list[kMaxTopK];
   int ctx;
-  float m[4][16];      // per wave (up to 4)
-  float l[4][16];
-  float o[4][16][D];
+  float m[NW][16];
+  float l[NW][16];
+  float o[NW][16][D];
 };
 
-template <int FMT, int D, int AUX>
-__global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(const AttendArgs a) {
+// UPW units (row, kv head, split) per workgroup.  UPW = 1: the workgroup's
+// 3 or 4 waves (blockDim) all serve its unit.  UPW = 4 (NVFP4 pages): 3 waves
+// per unit, 12 per workgroup, so that a workgroup fills one CU at 3 waves per
+// SIMD and the LDS of four units keeps a second one off it: the grid is
+// placed whole in one round.  (Separate 3-wave workgroups leave some SIMDs
+// with fewer waves than others, and on a machine filled to 3 per SIMD a few
+// workgroups then find no SIMDs to start on until others finish.)  Units past
+// the last one take part in the barriers only.
+template <int FMT, int D, int AUX, int UPW>
+__global__ __launch_bounds__(UPW == 1 ? 256 : 192 * UPW, kWavesPerSimd<FMT>) void attend_rows_kernel(const AttendArgs a) {
   constexpr int KK = D / 32, NN = D / 16, NB = kStages<FMT>;
+  constexpr int NWMAX = UPW == 1 ? 4 : 3;
   typedef typename OpType<FMT>::type OT;
-  __shared__ AttendSmem<D> sm;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int nw = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);   // waves of the workgroup (3 or 4)
+  __shared__ AttendSmem<D, NWMAX> smem[UPW];
+  const int wave_wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // waves per unit (3 or 4), this wave's unit and its index among the unit's waves
+  const int nw = UPW == 1 ? __builtin_amdgcn_readfirstlane(blockDim.x >> 6) : 3;
+  const int unit = UPW == 1 ? 0 : wave_wg / 3;
+  const int wave = wave_wg - unit * nw;
+  AttendSmem<D, NWMAX>& sm = smem[unit];
   const int r = lane & 15, g = lane >> 4;
-  int bid = blockIdx.x;
+  const int64_t units = (int64_t)a.total_rows * a.num_kv_heads * a.nsplit;
+  const int64_t uid = (int64_t)blockIdx.x * UPW + unit;
+  const bool live = uid < units;
+  int bid = (int)(live ? uid : 0);
   const int split = bid % a.nsplit;
   bid /= a.nsplit;
   const int kvh = bid % a.num_kv_heads;
@@ -478,7 +497,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
     if (lane == 0) sm.ctx = rs.ctx;
   }
   __syncthreads();
-  const int ctx = __builtin_amdgcn_readfirstlane(sm.ctx);
+  const int ctx = live ? __builtin_amdgcn_readfirstlane(sm.ctx) : 0;
   const int nchunks = (ctx + 31) >> 5;
   const int c0 = (int)((int64_t)nchunks * split / a.nsplit);
   const int c1 = (int)((int64_t)nchunks * (split + 1) / a.nsplit);
@@ -550,16 +569,16 @@ __global__ __launch_bounds__(256, kWavesPerSimd<FMT>) void attend_rows_kernel(co
   }
   __syncthreads();
   const float vscale = a.v_scale ? *a.v_scale : 1.f;
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += nw * 64) {
+  for (int idx = wave * 64 + lane; live && idx < G * (D / 4); idx += nw * 64) {
     const int h = idx / (D / 4), d = (idx % (D / 4)) * 4;
     float M = sm.m[0][h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < NWMAX; ++w)
       if (w < nw) M = fmaxf(M, sm.m[w][h]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWMAX; ++w) {
       if (w >= nw) break;
       const float e = exp2_fast(sm.m[w][h] - Mu);
       L += sm.l[w][h] * e;
@@ -733,22 +752,41 @@ static int choose_waves(int64_t units, int waves_per_simd, int cus) {
   return best;
 }
 
+// Units per workgroup: 4 (3 waves each) for a grid of 3-wave units that
+// needs more than 3 and at most 4 per CU, which then runs as one 12-wave
+// workgroup per CU; 1 otherwise.
+static int choose_units_per_wg(int64_t units, int nw, int cus) {
+  const int64_t c = cus > 0 ? cus : 256;
+  return nw == 3 && units > 3 * c && units <= 4 * c ? 4 : 1;
+}
+
 template <int FMT, int D>
 static hipError_t launch_fmt(const AttendArgs& a, int rows, hipStream_t stream) {
-  const int64_t blocks = (int64_t)rows * a.num_kv_heads * a.nsplit;
-  const int nw = choose_waves(blocks, kWavesPerSimd<FMT>, a.num_cus);
+  const int64_t units = (int64_t)rows * a.num_kv_heads * a.nsplit;
+  const int nw = choose_waves(units, kWavesPerSimd<FMT>, a.num_cus);
+  const int upw = kWavesPerSimd<FMT> >= 3 ? choose_units_per_wg(units, nw, a.num_cus) : 1;
+  const unsigned grid = (unsigned)((units + upw - 1) / upw);
   // With one query row per request each page is read by exactly one
   // workgroup: stream it past the caches.  Several rows of a request (a
   // multi-token decode) select overlapping blocks, which the L2 then serves
   // to the neighbouring rows.
   const bool streamed = a.dql == 1;
-  log_launch("attend_rows_kernel decode, %s pages, head_dim %d: %lld workgroups (row x kv head x split) of %d waves, "
-             "%d split%s, %s loads", FMT == kFmtBf16 ? "bf16" : (FMT == kFmtFp8 ? "fp8" : "nvfp4"), D,
-             (long long)blocks, nw, a.nsplit, a.nsplit == 1 ? "" : "s", streamed ? "streaming" : "cached");
-  if (streamed)
-    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, kStreamLoads>), dim3((unsigned)blocks), dim3(64 * nw), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, 0>), dim3((unsigned)blocks), dim3(64 * nw), 0, stream, a);
+  log_launch("attend_rows_kernel decode, %s pages, head_dim %d: %lld units (row x kv head x split) of %d waves, "
+             "%d per workgroup (%u workgroups), %d split%s, %s loads",
+             FMT == kFmtBf16 ? "bf16" : (FMT == kFmtFp8 ? "fp8" : "nvfp4"), D, (long long)units, nw, upw, grid,
+             a.nsplit, a.nsplit == 1 ? "" : "s", streamed ? "streaming" : "cached");
+  if (upw == 4) {
+    if constexpr (kWavesPerSimd<FMT> >= 3) {
+      if (streamed)
+        hipLaunchKernelGGL((attend_rows_kernel<FMT, D, kStreamLoads, 4>), dim3(grid), dim3(64 * 3 * 4), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attend_rows_kernel<FMT, D, 0, 4>), dim3(grid), dim3(64 * 3 * 4), 0, stream, a);
+    }
+  } else if (streamed) {
+    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, kStreamLoads, 1>), dim3(grid), dim3(64 * nw), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attend_rows_kernel<FMT, D, 0, 1>), dim3(grid), dim3(64 * nw), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int pairs = rows * a.num_q_heads;

@@ -269,6 +269,24 @@ def test_decode_parity_full_size_every_row(name):
     _parity(make_workload(name))
 
 
+@pytest.mark.parametrize("kw", [
+    dict(num_reqs=1021, Hq=8, Hkv=1, seq_range=(200, 3000), seed=91),      # last workgroup: 1 live unit
+    dict(num_reqs=1023, Hq=16, Hkv=1, seq_range=(200, 3000), seed=92),     # last workgroup: 3 live units
+    dict(num_reqs=50, seq_range=(1000, 6000), seed=93),                    # 400 row-heads in 2 splits
+    dict(num_reqs=400, dql=2, Hq=8, Hkv=1, seq_range=(200, 3000), seed=94),  # cached loads (dql 2)
+])
+def test_decode_nvfp4_twelve_wave_workgroups(kw, capfd, monkeypatch):
+    # NVFP4 decode grids of more than 3 and at most 4 units (row x kv head x
+    # split) per CU run four units per 12-wave workgroup, the units past the
+    # last one idle; each row matches the oracle
+    monkeypatch.setenv("MSA_LOG", "1")
+    capfd.readouterr()
+    _parity(make_workload("C5s", **kw))
+    err = capfd.readouterr().err
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert "4 per workgroup" in err, err
+
+
 def _c4_stratified_rows(wl, seed=7, n_random=1024):
     """Every row of the first request and every padded row; for the other
     requests the first and last row of every 32-row query tile (so of every
