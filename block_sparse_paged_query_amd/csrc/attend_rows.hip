@@ -539,6 +539,18 @@ __global__ __launch_bounds__(UPW == 1 ? 256 : 192 * UPW, kWavesPerSimd<FMT>) voi
   // nothing), so every path has the same outstanding loads and each chunk
   // waits only for its own.
   for (int j = 0; j < n_w; j += NB) {
+    if constexpr (UPW > 1) {
+      // One-round grid: all waves start together and the launch ends with
+      // the last.  Issue priority by remaining work (3 for the first quarter
+      // of a wave's chunks, down to 0 for the last) lets lagging waves issue
+      // before leading ones; by default the oldest waves of a CU win issue
+      // and finish far ahead of the youngest.
+      const int p = min(3, (4 * (n_w - j)) / n_w);
+      if (p == 3) __builtin_amdgcn_s_setprio(3);
+      else if (p == 2) __builtin_amdgcn_s_setprio(2);
+      else if (p == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int c = cw + nw * (j + b);
@@ -554,6 +566,7 @@ __global__ __launch_bounds__(UPW == 1 ? 256 : 192 * UPW, kWavesPerSimd<FMT>) voi
     }
   }
 
+  if constexpr (UPW > 1) __builtin_amdgcn_s_setprio(0);
   // merge the waves through LDS
   const float lsum = st.lacc[0];
   if (r < G) {
