@@ -9,27 +9,31 @@
 // [SPA] vllm.models.minimax_m3.amd.ops.sparse_pa,
 //      _write_sparse_block_table_row_from_values (the tokens a row sees).
 //
-// Work decomposition.  A workgroup (8 waves) owns one kv head and QT
-// consecutive query rows of one request (QT = 16 RT, RT = floor(16 / G) rows
-// per matrix tile for G query heads per kv head: 16 rows at G >= 9, 256 at
-// G = 1; a tile's 16 - RT G spare columns stay masked).  Every query row picks its own
+// Work decomposition.  A workgroup (16 waves, four per SIMD) owns one kv head
+// and QT consecutive query rows of one request (QT = 16 RT, RT = floor(16 / G)
+// rows per matrix tile for G query heads per kv head: 16 rows at G >= 9, 256
+// at G = 1; a tile's 16 - RT G spare columns stay masked).  Every query row picks its own
 // blocks, so the workgroup first builds, per block of the request, the bit
 // mask of its rows that selected it (and may see it causally), then walks
 // the blocks some row selected in ascending order (a window of blocks at a
 // time for long contexts).  Each such block's K and V (128 keys x D bf16)
-// go once into LDS by direct-to-LDS buffer loads (a scalar descriptor per
-// block, 32-bit lane offsets; each lane's LDS slot is fixed, so layouts are
-// made by choosing which global chunk a lane fetches),
+// go once into LDS by direct-to-LDS buffer loads issued by waves 0-7 (a
+// scalar descriptor per block, 32-bit lane offsets; each lane's LDS slot is
+// fixed, so layouts are made by choosing which global chunk a lane fetches),
 // double-buffered: K as [key][d] with 16-byte chunks XOR-swizzled by key, V
 // as [d pair of 16-byte chunks][key] so that the transposing read
 // ds_read_b64_tr_b16 (a lane receives one column of the 4 key rows its
 // 16-lane group points at) yields the V^T operand with no bank conflict.
 // The next block's copies are all issued when a block starts, into the other
-// buffer, so they have the whole block's compute to land.  Every wave owns 2
-// matrix tiles of 16 rows = (16 / G query rows) x (G heads) and runs
-// QK^T and PV only for the tiles whose rows selected the block; the other
-// rows of an active tile are masked.  Online softmax state stays in
-// registers; the workgroup writes its rows' bf16 outputs at the end.
+// buffer, so they have the whole block's compute to land.  Every wave owns one
+// matrix tile of 16 columns = (16 / G query rows) x (G heads) and runs QK^T and
+// PV only when a row of its tile selected the block; the other rows of an
+// active tile are masked.  One tile per wave keeps a wave within 128 VGPRs, so
+// four waves share each SIMD: a SIMD's active tiles sit in different waves
+// and overlap, instead of running one after the other inside a wave.  Each
+// chunk's K and V operands are read from LDS just before use (the other
+// waves cover the latency).  Online softmax state stays in registers; the
+// workgroup writes its rows' bf16 outputs at the end.
 // Workgroups of one kv head share an XCD (blockIdx % Hkv), so K/V blocks
 // re-read by neighbouring query tiles hit that XCD's L2.
 //
@@ -49,9 +53,11 @@
 
 namespace msa {
 
-constexpr int kPfWaves = 8;                 // two per SIMD: one's softmax overlaps the other's MFMAs
+constexpr int kPfWaves = 16;                // four per SIMD
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfTiles = 2;                 // matrix tiles per wave
+constexpr int kPfTiles = 1;                 // matrix tiles per wave
+constexpr int kPfCopyWaves = 8;             // waves that copy, stage and convert K/V blocks
+constexpr int kPfCopyThreads = 64 * kPfCopyWaves;
 // Row masks: a workgroup tile has QT = 16 RT rows (32 for 8 query heads per
 // kv head, 80 for 3, 256 for 1), so a block's mask is MW = ceil(QT / 32)
 // words; the block masks of a window of kPfWindow<MW> blocks are held at once
@@ -99,7 +105,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // (d = 8 lc .. 8 lc + 7) of key.
 
 // The copy of block `phys` (logical block `blk`), kv head kvh, into LDS
-// (kb, vb): each wave copies one 16-token page of K and an eighth of V,
+// (kb, vb), by waves 0-7: each copies one 16-token page of K and an eighth of V,
 // D / 32 instructions of 1 KB for each side.  K instruction (wave, part)
 // holds keys 16 wave + (64 / L) part + lane / L (L = D / 8 lanes per key
 // row); V instruction v = wave * (D / 32) + part holds keys 32 (v % 4) +
@@ -111,6 +117,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ void pf_issue_block(lds_u8* kb, lds_u8* vb, const AttendArgs& a, int kvh, int phys,
                                                int blk, int seq_len) {
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kPfCopyWaves) return;
   constexpr int L = D / 8, KPI = 64 / L, PARTS = D / 32;
   // (block ids come from LDS: make their uniformity explicit so that the
   // bases below are scalar and only 32-bit lane offsets stay in registers)
@@ -163,7 +170,7 @@ struct PfWave {
   static constexpr int KK = D / 32, NN = D / 16;
   OT qop[kPfTiles][KK];
   f32x4 acc[kPfTiles][NN];
-  f32x4 lacc[kPfTiles];   // softmax denominators: P times an all-ones operand
+  float lsum[kPfTiles];   // softmax denominators: this lane's share (its 8 keys of each chunk)
   float m[kPfTiles];
   int lrow[kPfTiles];     // row within the workgroup tile, or -1
   int lbit[kPfTiles];     // its bit in the wave's block mask
@@ -173,24 +180,33 @@ struct PfWave {
 // Online softmax keeps, per (row, head), a reference max m and rescales the
 // accumulators only when some lane's chunk max exceeds m by more than kLazy
 // (log2 units): probabilities are then at most 2^kLazy, well inside bf16 /
-// fp32 range.  The common case needs no cross-lane max and no rescale; the
-// denominator is accumulated by the matrix core (P times a ones operand), so
-// it sums exactly the bf16 probabilities the PV product uses.
+// fp32 range.  The common case needs no cross-lane max and no rescale.  Each
+// lane sums the rounded probabilities it feeds the PV product (two per dot
+// instruction), so the denominator sums exactly what the products use; the
+// four lanes of a column are added at the end.
 constexpr float kLazy = 8.f;
+
+// acc + the two probabilities packed in w (a bf16 or fp16 pair)
+template <class PT>
+__device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
+  if constexpr (__is_same(PT, f16x8)) {
+    return __builtin_amdgcn_fdot2(bits_f16x2(w), bits_f16x2(0x3c003c00u), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                           acc, false);
+  }
+}
 
 // One 32-key chunk against the tiles in MASK (a compile-time set, so that the
 // phases below form straight-line code): all QK^T products, then all
 // softmaxes (one uniform branch covers the rare rescale of any tile), then all
-// PV products.  A tile's softmax runs while the next tile's products are in
-// the matrix pipe, and its PV products while the next softmax runs.
-// `next_k` / `next_v` refill the K / V operand registers with the next
-// chunk's once this chunk's products have consumed them, so those LDS reads
-// overlap this chunk's softmax and PV work instead of stalling the next
-// chunk's first product.
-template <int MASK, int D, class OT, class PT, class NextK, class NextV>
-__device__ __forceinline__ void pf_chunk(PfWave<OT, D>& w, OT (&kop)[2][PfWave<OT, D>::KK],
-                                         PT (&vop)[PfWave<OT, D>::NN], const float (&bias)[kPfTiles], const PT& ones,
-                                         float sl2, bool causal, int kbase, NextK&& next_k, NextV&& next_v) {
+// PV products.  `read_v` reads this chunk's V operands once the QK^T products
+// have consumed the K operands (into registers the K operands no longer
+// need), so those LDS reads overlap the softmax.
+template <int MASK, int D, class OT, class PT, class ReadV>
+__device__ __forceinline__ void pf_chunk(PfWave<OT, D>& w, const OT (&kop)[2][PfWave<OT, D>::KK],
+                                         PT (&vop)[PfWave<OT, D>::NN], const float (&bias)[kPfTiles], float sl2,
+                                         bool causal, int kbase, ReadV&& read_v) {
   constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN;
   constexpr bool kF16 = __is_same(PT, f16x8);
   float sv[kPfTiles][8];
@@ -209,8 +225,8 @@ __device__ __forceinline__ void pf_chunk(PfWave<OT, D>& w, OT (&kop)[2][PfWave<O
       sv[i][4 + ii] = s1[ii];
     }
   }
-  __builtin_amdgcn_sched_barrier(0);   // the refill must not rise above the products reading kop
-  next_k(kop);
+  __builtin_amdgcn_sched_barrier(0);   // the V reads must not rise above the products reading kop
+  read_v(vop);
   float mxs[kPfTiles];
   bool need = false;
 #pragma unroll
@@ -241,7 +257,7 @@ __device__ __forceinline__ void pf_chunk(PfWave<OT, D>& w, OT (&kop)[2][PfWave<O
       const float alpha = exp2_fast(w.m[i] - (m_new == -INFINITY ? 0.f : m_new));
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = w.acc[i][nn] * alpha;
-      w.lacc[i] = w.lacc[i] * alpha;
+      w.lsum[i] *= alpha;
       w.m[i] = m_new;
     }
   }
@@ -261,10 +277,9 @@ __device__ __forceinline__ void pf_chunk(PfWave<OT, D>& w, OT (&kop)[2][PfWave<O
     const PT pop = __builtin_bit_cast(PT, pw);
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = mfma16(vop[nn], pop, w.acc[i][nn]);
-    w.lacc[i] = mfma16(ones, pop, w.lacc[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w.lsum[i] = dot2_ones<PT>(pw[e], w.lsum[i]);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  next_v(vop);
 }
 
 struct PfNext {       // the block whose copies are issued during this one
@@ -275,13 +290,13 @@ struct PfNext {       // the block whose copies are issued during this one
 };
 
 // The block's four 32-key chunks against the tiles in MASK.  Each chunk's K
-// and V operands (shared by the wave's active tiles) are read from LDS while
-// the previous chunk computes.
+// operands are read from LDS when the chunk starts and its V operands after
+// its QK^T products; a wave holds one chunk's operands at a time, and the
+// other waves of its SIMD cover the read latency.
 template <int MASK, int D, class OT, class PT>
 __device__ __forceinline__ void pf_chunks(PfWave<OT, D>& w, const uint8_t* kb, const uint8_t* vb,
                                           const int (&koff)[PfWave<OT, D>::KK], int voff,
-                                          const float (&bias)[kPfTiles], const PT& ones, float sl2, bool causal,
-                                          int kbase0) {
+                                          const float (&bias)[kPfTiles], float sl2, bool causal, int kbase0) {
   constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN;
   auto load_k = [&](OT (&kop)[2][KK], int c) {
 #pragma unroll
@@ -303,13 +318,11 @@ __device__ __forceinline__ void pf_chunks(PfWave<OT, D>& w, const uint8_t* kb, c
   };
   OT kop[2][KK];
   PT vop[NN];
-  load_k(kop, 0);
-  load_v(vop, 0);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    pf_chunk<MASK, D, OT, PT>(w, kop, vop, bias, ones, sl2, causal, kbase0 + c * 32,
-                       [&](OT (&k)[2][KK]) { if (c < 3) load_k(k, c + 1); },
-                       [&](PT (&v)[NN]) { if (c < 3) load_v(v, c + 1); });
+    load_k(kop, c);
+    pf_chunk<MASK, D, OT, PT>(w, kop, vop, bias, sl2, causal, kbase0 + c * 32,
+                              [&](PT (&v)[NN]) { load_v(v, c); });
   }
 }
 
@@ -317,15 +330,14 @@ __device__ __forceinline__ void pf_chunks(PfWave<OT, D>& w, const uint8_t* kb, c
 // rows that selected the block (bit i * RT + k: row k of tile i).  `causal`
 // is set when the block can be the own block of a row of this workgroup
 // (keys past a row's position must be masked); earlier blocks need only the
-// row selection.  Every wave first issues its pieces of the next block's
+// row selection.  Waves 0-7 first issue their pieces of the next block's
 // copies, active or not.
 template <int D, class OT, class PT>
 __device__ __forceinline__ void pf_compute_block(PfWave<OT, D>& w, const uint8_t* kb, const uint8_t* vb,
                                                  uint32_t bmask, int blk, int RT, float sl2, bool causal,
                                                  const PfNext& nx, const AttendArgs& a, int kvh, int seq_len) {
-  constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN;
-  constexpr bool kF16 = __is_same(PT, f16x8);
-  static_assert(kPfTiles == 2, "the tile sets below enumerate two tiles");
+  constexpr int KK = PfWave<OT, D>::KK;
+  static_assert(kPfTiles == 1, "one matrix tile per wave");
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   // per-lane LDS offsets (chunk / tile / step parts are compile-time)
   int koff[KK];
@@ -346,19 +358,15 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT, D>& w, const uint8_t
     bias[i] = sel ? 0.f : -INFINITY;
   }
   const int kpos_blk = blk * kBlockTokens;
-  const uint32_t one2 = kF16 ? 0x3c003c00u : 0x3f803f80u;   // 1.0 x 2 in the operand type
-  const PT ones = __builtin_bit_cast(PT, u32x4{one2, one2, one2, one2});
   if (nx.valid) pf_issue_block<D>(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len);
-  if (tiles == 3) pf_chunks<3, D, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
-  else if (tiles == 1) pf_chunks<1, D, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
-  else if (tiles == 2) pf_chunks<2, D, OT, PT>(w, kb, vb, koff, voff, bias, ones, sl2, causal, kpos_blk + 4 * g);
+  if (tiles) pf_chunks<1, D, OT, PT>(w, kb, vb, koff, voff, bias, sl2, causal, kpos_blk + 4 * g);
 }
 
 // ---- staged formats -------------------------------------------------------
 //
 // Copy of one block's raw bytes (kv head kvh) into the staging buffer `raw`,
-// spread over the workgroup: each wave instruction fills 64 consecutive
-// 16-byte slots, a lane's source being any 16-byte piece.
+// spread over waves 0-7: each wave instruction fills 64 consecutive 16-byte
+// slots, a lane's source being any 16-byte piece.
 //   fp8:   K as [key][D B] (piece (key, n) at key * D / 16 + n), then V as
 //          [n][key] (piece 8 D + n * 128 + key) so that the conversion
 //          writes the V layout with consecutive lanes on consecutive keys.
@@ -369,7 +377,9 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT, D>& w, const uint8_t
 template <int FMT, int D>
 __device__ __forceinline__ void pf_stage_issue(lds_u8* raw, const AttendArgs& a, int kvh, int phys) {
   constexpr int NPK = D / 16, HALF = kBlockTokens * NPK;   // pieces per key row; K pieces
+  constexpr int kPfThreads = kPfCopyThreads;              // (the loops below run on waves 0-7)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= kPfCopyWaves) return;
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));   // recompute the lane offsets here rather than keep them live across blocks
   phys = __builtin_amdgcn_readfirstlane(phys);
@@ -466,6 +476,8 @@ __device__ __forceinline__ void pf_stage_item(const uint8_t* raw, bool v_side, i
 template <int FMT, int D>
 __device__ __forceinline__ void pf_stage_convert(const uint8_t* raw, uint8_t* kc, uint8_t* vc, int nkeys) {
   constexpr int NPK = D / 16, HALF = kBlockTokens * NPK;
+  constexpr int kPfThreads = kPfCopyThreads;              // waves 0-7 convert
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kPfCopyWaves) return;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));    // as in the copy issue: offsets recomputed per block
 #pragma unroll
@@ -501,6 +513,7 @@ __device__ __forceinline__ void pf_convert_own_page(const uint8_t* raw, uint8_t*
                                                     int part) {
   static_assert(D == 128, "NVFP4 pages hold head_dim 128");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= kPfCopyWaves) return;   // waves 0-7 copied the block's 8 pages
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));
   const bool v_side = part >= 2;
@@ -619,7 +632,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   const int nrows = row_end - row0;
 
   // ---- this wave's query operands and row data.  The wave's rows are
-  // 2 RT consecutive ones, bits [wbit0, wbit0 + 2 RT) of a block's mask.
+  // RT consecutive ones, bits [wbit0, wbit0 + RT) of a block's mask.
   PfWave<OT, D> w;
   const int wbit0 = wave * kPfTiles * RT;
 #pragma unroll
@@ -630,7 +643,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
     w.lbit[i] = rr - wbit0;
     w.lpos[i] = pos_first + rr;
     w.m[i] = -INFINITY;
-    w.lacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    w.lsum[i] = 0.f;
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
                           (((int64_t)(row0 + (ok ? rr : 0)) * a.num_q_heads + kvh * G + (r % G)) * D) * 2;
 #pragma unroll
@@ -698,7 +711,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
     auto wave_mask = [&](int jl) -> uint32_t {
       uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane(s_mask[jl][wword]) >> wshift;
       if constexpr (MW > 1) {
-        // a wave's 2 RT bits run into the next word when 2 RT does not divide 32
+        // a wave's RT bits run into the next word when RT does not divide 32
         if (wshift + kPfTiles * RT > 32)
           m |= (uint32_t)__builtin_amdgcn_readfirstlane(s_mask[jl][wword + 1]) << (32 - wshift);
       }
@@ -806,7 +819,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   const float vscale = a.v_scale ? *a.v_scale : 1.f;
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
-    const float L = w.lacc[i][0];      // every entry holds the head's full sum
+    // the head's denominator: the four lanes of its column hold a quarter of the keys each
+    float L = w.lsum[i];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
     if (w.lrow[i] < 0) continue;
     const float inv = L > 0.f ? vscale / L : 0.f;
     uint8_t* orow = reinterpret_cast<uint8_t*>(a.out) +
@@ -951,7 +967,7 @@ hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t strea
   const int n_slots = (a.total_rows + QT - 1) / QT + a.num_reqs + 2;
   const dim3 grid((unsigned)((int64_t)n_slots * a.num_kv_heads));
   log_launch("prefill_blocks_kernel %s pages, head_dim %d, %d query heads per kv head: %d tiles of %d rows x %d kv "
-             "heads, 8 waves each", fmt == kFmtBf16 ? "bf16" : (fmt == kFmtFp8 ? "fp8" : "nvfp4"), a.head_dim,
+             "heads, 16 waves each", fmt == kFmtBf16 ? "bf16" : (fmt == kFmtFp8 ? "fp8" : "nvfp4"), a.head_dim,
              a.group, n_slots, QT, a.num_kv_heads);
   if (a.head_dim == 128) {
     if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 128>(a, grid, n_slots, stream);
