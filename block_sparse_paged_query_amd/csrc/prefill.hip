@@ -175,6 +175,7 @@ struct PfWave {
   int lrow[kPfTiles];     // row within the workgroup tile, or -1
   int lbit[kPfTiles];     // its bit in the wave's block mask
   int lpos[kPfTiles];     // that row's absolute position
+  int last_pos;           // the wave's last row position (uniform), -1 without rows
 };
 
 // Online softmax keeps, per (row, head), a reference max m and rescales the
@@ -296,7 +297,8 @@ struct PfNext {       // the block whose copies are issued during this one
 template <int MASK, int D, class OT, class PT>
 __device__ __forceinline__ void pf_chunks(PfWave<OT, D>& w, const uint8_t* kb, const uint8_t* vb,
                                           const int (&koff)[PfWave<OT, D>::KK], int voff,
-                                          const float (&bias)[kPfTiles], float sl2, bool causal, int kbase0) {
+                                          const float (&bias)[kPfTiles], float sl2, bool causal, int kbase0,
+                                          int nch) {
   constexpr int KK = PfWave<OT, D>::KK, NN = PfWave<OT, D>::NN;
   auto load_k = [&](OT (&kop)[2][KK], int c) {
 #pragma unroll
@@ -320,6 +322,7 @@ __device__ __forceinline__ void pf_chunks(PfWave<OT, D>& w, const uint8_t* kb, c
   PT vop[NN];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
+    if (c >= nch) break;   // chunks past the wave's last row hold only masked keys
     load_k(kop, c);
     pf_chunk<MASK, D, OT, PT>(w, kop, vop, bias, sl2, causal, kbase0 + c * 32,
                               [&](PT (&v)[NN]) { load_v(v, c); });
@@ -359,7 +362,10 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT, D>& w, const uint8_t
   }
   const int kpos_blk = blk * kBlockTokens;
   if (nx.valid) pf_issue_block<D>(nx.kb, nx.vb, a, kvh, nx.phys, nx.blk, seq_len);
-  if (tiles) pf_chunks<1, D, OT, PT>(w, kb, vb, koff, voff, bias, sl2, causal, kpos_blk + 4 * g);
+  // in a row's own block, the chunks past the wave's last row are masked for
+  // all of the wave's rows
+  const int nch = causal ? min(4, (w.last_pos - kpos_blk) / 32 + 1) : 4;
+  if (tiles) pf_chunks<1, D, OT, PT>(w, kb, vb, koff, voff, bias, sl2, causal, kpos_blk + 4 * g, nch);
 }
 
 // ---- staged formats -------------------------------------------------------
@@ -656,6 +662,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
     }
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) w.acc[i][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  {
+    int lp = w.lrow[0] >= 0 ? w.lpos[0] : -1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) lp = max(lp, __shfl_xor(lp, o));
+    w.last_pos = __builtin_amdgcn_readfirstlane(lp);
   }
   const float kscale = a.k_scale ? *a.k_scale : 1.f;
   const float sl2 = a.softmax_scale * kscale * kLog2e;
