@@ -323,6 +323,14 @@ __device__ __forceinline__ void pf_chunks(PfWave<OT, D>& w, const uint8_t* kb, c
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     if (c >= nch) break;   // chunks past the wave's last row hold only masked keys
+    // Issue priority from the work left in the block (3 in the first chunk, 0
+    // in the last): a CU issues from its oldest waves first, which would let
+    // them run ahead and leave the youngest to finish the block alone, with
+    // nothing to hide its latency; the block's barrier waits for that one.
+    if (c == 0) __builtin_amdgcn_s_setprio(3);
+    else if (c == 1) __builtin_amdgcn_s_setprio(2);
+    else if (c == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     load_k(kop, c);
     pf_chunk<MASK, D, OT, PT>(w, kop, vop, bias, sl2, causal, kbase0 + c * 32,
                               [&](PT (&v)[NN]) { load_v(v, c); });
@@ -366,6 +374,7 @@ __device__ __forceinline__ void pf_compute_block(PfWave<OT, D>& w, const uint8_t
   // all of the wave's rows
   const int nch = causal ? min(4, (w.last_pos - kpos_blk) / 32 + 1) : 4;
   if (tiles) pf_chunks<1, D, OT, PT>(w, kb, vb, koff, voff, bias, sl2, causal, kpos_blk + 4 * g, nch);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // ---- staged formats -------------------------------------------------------
@@ -765,6 +774,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
       // compute buffers and issues block i+2's copy: one barrier per block.
       const PfNext none = {nullptr, nullptr, 0, 0, false};
       auto convert = [&](int idx, uint8_t* kc, uint8_t* vc) {
+        // the next block's conversion goes ahead of the other waves' chunks
+        // (the chunks then set their own priority)
+        __builtin_amdgcn_s_setprio(3);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's copy of its page has landed
         const int nk = seq_len - (w0 + (int)s_list[idx]) * kBlockTokens;
 #pragma unroll
