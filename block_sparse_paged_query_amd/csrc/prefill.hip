@@ -32,8 +32,12 @@
 // four waves share each SIMD: a SIMD's active tiles sit in different waves
 // and overlap, instead of running one after the other inside a wave.  Each
 // chunk's K and V operands are read from LDS just before use (the other
-// waves cover the latency).  Online softmax state stays in registers; the
-// workgroup writes its rows' bf16 outputs at the end.
+// waves cover the latency).  Every block ends at a workgroup barrier, so each
+// wave sets its issue priority from the work it has left in the block, which
+// keeps a SIMD's waves in step instead of leaving the youngest to finish
+// alone.  In a row's own block, the 32-key chunks past the wave's last row
+// are skipped.  Online softmax state stays in registers; the workgroup
+// writes its rows' bf16 outputs at the end.
 // Workgroups of one kv head share an XCD (blockIdx % Hkv), so K/V blocks
 // re-read by neighbouring query tiles hit that XCD's L2.
 //
@@ -41,10 +45,12 @@
 // for the two NVFP4 slots) take a staged path: the selected block's raw bytes
 // (half or a quarter of bf16's) go into LDS and are converted exactly (fp8 ->
 // bf16; e2m1 x E4M3 block scale -> fp16) into the same K / V layouts the
-// bf16 path reads, so the matrix-core loop is shared.  fp8 stages into two
-// raw buffers and converts each block at its start; NVFP4 (a smaller raw
-// block) keeps two compute-layout buffers and converts the next block while
-// the current one computes, each wave converting the page it copied.  NVFP4
+// bf16 path reads, so the matrix-core loop is shared.  Waves 0-7 copy and
+// convert, so the other waves of each SIMD keep computing meanwhile.  fp8
+// stages into two raw buffers and converts each block at its start; NVFP4 (a
+// smaller raw block) keeps two compute-layout buffers and converts the next
+// block while the current one computes, each wave converting the page it
+// copied, at raised priority.  NVFP4
 // computes in fp16 (the query is converted once), fp8 in bf16; the
 // per-tensor scales fold into the softmax scale and the output as in the
 // decode.
