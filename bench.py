@@ -437,9 +437,12 @@ def measure(args, torch, msa, dev, keep_inputs):
                                   decode_query_len=wl.decode_query_len, out=out, workspace=ws)
     else:
         work = 4.0 * wl.head_dim * wl.num_q_heads * sum_ctx                                   # flops
+        ws = torch.empty(max(msa.msa_prefill_workspace_size(wl.total_q, wl.num_q_heads, wl.head_dim, wl.topk_k), 1),
+                         dtype=torch.uint8, device=dev)
 
         def step(i):
-            msa.msa_sparse_prefill(q, layers[i % len(layers)], topk, bt, cu, seq, wl.softmax_scale, out=out)
+            msa.msa_sparse_prefill(q, layers[i % len(layers)], topk, bt, cu, seq, wl.softmax_scale, out=out,
+                                   workspace=ws)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):

@@ -29,7 +29,7 @@ __all__ = [
     "MsaError", "KVCache", "library_path", "load_library",
     "msa_build_sparse_block_table", "msa_query_token_positions",
     "msa_sparse_decode", "msa_sparse_decode_noalloc", "msa_sparse_prefill", "msa_sparse_attention", "msa_insert_index_cache",
-    "msa_debug_gather_dequant", "msa_decode_workspace_size",
+    "msa_debug_gather_dequant", "msa_decode_workspace_size", "msa_prefill_workspace_size",
     "MSA_BF16", "MSA_FP16", "MSA_FP8_E4M3FN", "MSA_NVFP4", "MSA_FP32",
 ]
 
@@ -250,6 +250,10 @@ def msa_decode_workspace_size(total_q, num_q_heads, head_dim, topk_k):
     return load_library().msa_decode_workspace_size(total_q, num_q_heads, head_dim, topk_k)
 
 
+def msa_prefill_workspace_size(total_q, num_q_heads, head_dim, topk_k):
+    return load_library().msa_prefill_workspace_size(total_q, num_q_heads, head_dim, topk_k)
+
+
 def _check_q(q, name="q"):
     _need(q, name, torch.bfloat16, 3)
     if q.device.type != "cuda":
@@ -347,7 +351,7 @@ def msa_sparse_prefill(q, kv: KVCache, topk, block_table, cu_seqlens_q, seq_lens
     if cu_seqlens_q.shape[0] != seq_lens.shape[0] + 1:
         raise ValueError("cu_seqlens_q must have num_reqs + 1 entries")
     if workspace is None:
-        nbytes = load_library().msa_prefill_workspace_size(total_q, hq, d, topk.shape[1])
+        nbytes = msa_prefill_workspace_size(total_q, hq, d, topk.shape[1])
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     kvs = kv._struct()
     _call("msa_sparse_prefill", _ptr(q), MSA_BF16, total_q, hq, ctypes.byref(kvs), _ptr(topk), topk.stride(0),
@@ -405,7 +409,9 @@ def msa_sparse_attention(q, kv: KVCache, topk, num_decode_tokens, softmax_scale,
             raise ValueError("prefill_cu_seqlens_q must have num_prefill_reqs + 1 entries")
         pbt, pcu, psl = prefill_block_table, prefill_cu_seqlens_q, prefill_seq_lens
     if workspace is None:
-        nbytes = msa_decode_workspace_size(max(nd, 1), hq, d, topk.shape[1])
+        # the two parts run one after the other and reuse one workspace
+        nbytes = max(msa_decode_workspace_size(max(nd, 1), hq, d, topk.shape[1]),
+                     msa_prefill_workspace_size(num_tokens - nd, hq, d, topk.shape[1]))
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     kvs = kv._struct()
     _call("msa_sparse_attention", _ptr(q), MSA_BF16, num_tokens, hq, ctypes.byref(kvs), _ptr(topk), topk.stride(0),

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/msa.h"
@@ -443,12 +444,15 @@ MSA_API msa_status_t msa_sparse_decode_noalloc(const void* q, int32_t q_dtype, i
                      stream);
 }
 
+// One 32-byte row order per 32-row query tile.  A request of n rows has
+// ceil(n / 32) tiles, so total_q rows in any number of requests have at most
+// total_q + ceil(total_q / 32) tiles.
 MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim, int32_t topk_k) {
-  (void)total_q;
   (void)num_q_heads;
   (void)head_dim;
   (void)topk_k;
-  return 0;
+  if (total_q <= 0) return 0;
+  return 32 * ((size_t)total_q + ((size_t)total_q + 31) / 32);
 }
 
 // Prefill: validate every host-visible argument, then (if `launch`) enqueue.
@@ -456,7 +460,8 @@ static msa_status_t prefill_impl(bool launch, const void* q, int32_t q_dtype, in
                                  const msa_kv_cache_t* kv, const int32_t* topk, int64_t topk_row_stride,
                                  int32_t topk_k, const int32_t* block_table, int64_t bt_row_stride, int32_t bt_cols,
                                  int32_t num_reqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens,
-                                 float softmax_scale, void* out, hipStream_t stream) {
+                                 float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
   MSA_CHECK(total_q >= 0 && num_reqs >= 0, MSA_ERR_INVALID_ARGUMENT, "negative total_q %d or num_reqs %d", total_q,
             num_reqs);
   MSA_CHECK(total_q <= (1 << 24), MSA_ERR_UNSUPPORTED, "%d prefill rows: at most 2^24", total_q);
@@ -474,6 +479,10 @@ static msa_status_t prefill_impl(bool launch, const void* q, int32_t q_dtype, in
   a.num_reqs = num_reqs;
   a.dql = 1;
   a.total_rows = total_q;
+  if (workspace != nullptr && workspace_bytes >= 32) {
+    a.row_perm = static_cast<int8_t*>(workspace);
+    a.perm_cap = (int32_t)std::min<size_t>(workspace_bytes / 32, (size_t)INT32_MAX);
+  }
   return hip_status(msa::launch_prefill_blocks(a, fmt_of(kv->kv_dtype), stream), "prefill launch");
 }
 
@@ -483,10 +492,9 @@ MSA_API msa_status_t msa_sparse_prefill(const void* q, int32_t q_dtype, int32_t 
                                         int32_t bt_cols, int32_t num_reqs, const int32_t* cu_seqlens_q,
                                         const int32_t* seq_lens, float softmax_scale, void* out, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   return prefill_impl(true, q, q_dtype, total_q, num_q_heads, kv, topk, topk_row_stride, topk_k, block_table,
-                      bt_row_stride, bt_cols, num_reqs, cu_seqlens_q, seq_lens, softmax_scale, out, stream);
+                      bt_row_stride, bt_cols, num_reqs, cu_seqlens_q, seq_lens, softmax_scale, out, workspace,
+                      workspace_bytes, stream);
 }
 
 MSA_API msa_status_t msa_sparse_attention(
@@ -516,15 +524,17 @@ MSA_API msa_status_t msa_sparse_attention(
   if (st != MSA_OK) return st;
   st = prefill_impl(false, qp, q_dtype, np, num_q_heads, kv, tp, topk_row_stride, topk_k, prefill_block_table,
                     prefill_bt_row_stride, prefill_bt_cols, num_prefill_reqs, prefill_cu_seqlens_q, prefill_seq_lens,
-                    softmax_scale, op, stream);
+                    softmax_scale, op, nullptr, 0, stream);
   if (st != MSA_OK) return st;
   st = decode_impl(true, q, q_dtype, nd / decode_query_len, decode_query_len, num_q_heads, kv, topk, topk_row_stride,
                    topk_k, decode_block_table, decode_bt_row_stride, decode_bt_cols, decode_seq_lens, softmax_scale,
                    out, workspace, workspace_bytes, stream);
   if (st != MSA_OK) return st;
+  // (stream order: the decode's split-K merge has read its partials before
+  // the prefill reuses the workspace)
   return prefill_impl(true, qp, q_dtype, np, num_q_heads, kv, tp, topk_row_stride, topk_k, prefill_block_table,
                       prefill_bt_row_stride, prefill_bt_cols, num_prefill_reqs, prefill_cu_seqlens_q,
-                      prefill_seq_lens, softmax_scale, op, stream);
+                      prefill_seq_lens, softmax_scale, op, workspace, workspace_bytes, stream);
 }
 
 MSA_API msa_status_t msa_insert_index_cache(const void* index_k, int64_t k_stride0, int64_t k_stride1, int32_t n,

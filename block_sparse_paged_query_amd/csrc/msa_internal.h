@@ -54,6 +54,10 @@ struct AttendArgs {
   float* ws_o;    // [rows][Hq][nsplit][D]
   float* ws_ml;   // [rows][Hq][nsplit][2]
   int32_t num_cus;   // compute units of the device (launch shaping)
+  // Prefill at 6-8 query heads per kv head: 32 bytes of row order per query
+  // tile for perm_cap tiles (device workspace), or NULL to keep row order.
+  int8_t* row_perm;
+  int32_t perm_cap;
 };
 
 hipError_t launch_attend_decode(const AttendArgs& a, int fmt, int rows, hipStream_t stream);

@@ -251,7 +251,12 @@ MSA_API msa_status_t msa_sparse_decode_noalloc(
 /* Size of msa_sparse_decode_noalloc's per-device scratch array, in bytes. */
 MSA_API size_t msa_decode_noalloc_scratch_bytes(void);
 
-/* Bytes of workspace msa_sparse_prefill needs (0 today; reserved). */
+/*
+ * Bytes of workspace msa_sparse_prefill can use: 32 per 32-row query tile,
+ * sized for any split of total_q rows into requests (32 * (total_q +
+ * ceil(total_q / 32)); 0 for total_q <= 0).  The other arguments are
+ * accepted for symmetry with msa_decode_workspace_size and not used.
+ */
 MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
                                           int32_t topk_k);
 
@@ -271,6 +276,13 @@ MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, 
  * Same math, page formats and limits as
  * msa_sparse_decode (bf16, fp8 e4m3fn or NVFP4 pages; NVFP4 computes in
  * fp16).
+ *
+ * workspace: device memory the call may overwrite (no alignment needed), or
+ * NULL.  At 6 to 8 query heads per kv head the call first writes one 32-byte
+ * row order per query tile there (rows with alike top-k rows share matrix
+ * tiles, which saves products); tiles past workspace_bytes / 32 keep their
+ * natural order.  Any size gives the same results up to rounding; the
+ * output does not depend on what the workspace held before the call.
  */
 MSA_API msa_status_t msa_sparse_prefill(
     const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,
@@ -295,7 +307,10 @@ MSA_API msa_status_t msa_sparse_prefill(
  * prefill_cu_seqlens_q counted from the first prefill row; either part may
  * be empty.  Both parts are validated before anything is enqueued; then
  * they run in that order on `stream`, with no host synchronisation (the call
- * can be captured into a HIP graph).  workspace as for msa_sparse_decode.
+ * can be captured into a HIP graph).  workspace serves both parts in turn
+ * (the decode's split-K partials, then the prefill's row orders): the larger
+ * of msa_decode_workspace_size and msa_prefill_workspace_size is room for
+ * both.
  */
 MSA_API msa_status_t msa_sparse_attention(
     const void* q, int32_t q_dtype, int32_t num_tokens, int32_t num_q_heads,

@@ -248,3 +248,17 @@ def test_index_cache_binding_checks():
         msa.msa_insert_index_cache(k, torch.zeros((2, 8, 4), dtype=torch.bfloat16).transpose(1, 2), s)
     with pytest.raises(ValueError, match="GPU"):
         msa.msa_insert_index_cache(k, c, s)                           # host tensors never reach a kernel
+
+
+def test_prefill_workspace_covers_every_query_tile():
+    # msa_sparse_prefill keeps one 32-byte row order per 32-row query tile
+    # (a request of n rows has ceil(n / 32) tiles).  The size it asks for
+    # must cover any split of total_q rows into requests, down to one row each.
+    assert msa.msa_prefill_workspace_size(0, 64, 128, 16) == 0
+    rng = np.random.default_rng(5)
+    for total in (1, 31, 32, 33, 1000, 22592):
+        splits = [[total], [1] * total, rng.multinomial(total, np.ones(7) / 7).tolist(),
+                  [31] * (total // 31) + [total % 31]]
+        for lens in splits:
+            tiles = sum((n + 31) // 32 for n in lens)
+            assert 32 * tiles <= msa.msa_prefill_workspace_size(total, 64, 128, 16), (total, lens[:5])

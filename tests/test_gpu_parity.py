@@ -38,13 +38,14 @@ def _kv(wl, cache):
                        wl.block_page_stride, ks, vs, layout=cache.get("layout", "page16"))
 
 
-def _run(wl, cache, q):
+def _run(wl, cache, q, workspace=None):
     kv = _kv(wl, cache)
     topk, bt, seq = _dev(wl.topk), _dev(wl.block_table), _dev(wl.seq_lens)
     if wl.mode == "decode":
         out = msa.msa_sparse_decode(q, kv, topk, bt, seq, wl.softmax_scale, decode_query_len=wl.decode_query_len)
     else:
-        out = msa.msa_sparse_prefill(q, kv, topk, bt, _dev(wl.cu_seqlens_q), seq, wl.softmax_scale)
+        out = msa.msa_sparse_prefill(q, kv, topk, bt, _dev(wl.cu_seqlens_q), seq, wl.softmax_scale,
+                                     workspace=workspace)
     torch.cuda.synchronize()
     return out
 
@@ -185,10 +186,10 @@ def test_gather_dequant_exhaustive_codes():
 
 # ---------------------------------------------------------------- attention
 
-def _parity(wl, rows=None, cache=None):
+def _parity(wl, rows=None, cache=None, workspace=None):
     cache = make_kv_cache(wl, DEV) if cache is None else cache
     q = make_query(wl, DEV)
-    out = _run(wl, cache, q)
+    out = _run(wl, cache, q, workspace)
     req, pos = oracle_positions(wl)
     rows = np.arange(wl.total_q) if rows is None else np.asarray(rows)
     oc, bt, _, _ = compact_oracle_inputs(wl, cache, rows)
@@ -518,6 +519,75 @@ def test_decode_split_counts(name):
         got = out.float().cpu().numpy()
         ok, err, _, _ = attention_within_tolerance(got, want, ATOL)
         assert ok, f"workspace {None if ws is None else ws.numel()}: max abs error {err}"
+
+
+def _expected_row_orders(wl):
+    # The prefill's row pairing for two-row tiles, restated: per 32-row query
+    # tile (requests in order), each row's selected blocks that it may see
+    # (below the tile's block count), folded to 64 bits; the lowest unpaired
+    # row takes the unpaired row with the highest 6 |common| + 64 - |own|
+    # (the lowest on ties); pair p fills slots 2p and 2p + 1.  Tiles of at
+    # most two rows, or with no blocks, keep the natural order.
+    orders = []
+    cu, seq, bt_cols = wl.cu_seqlens_q, wl.seq_lens, wl.block_table.shape[1]
+    for r in range(len(seq)):
+        ctx0 = int(seq[r]) - int(cu[r + 1] - cu[r])
+        for t0 in range(int(cu[r]), int(cu[r + 1]), 32):
+            nrows = min(32, int(cu[r + 1]) - t0)
+            pos_first = ctx0 + t0 - int(cu[r])
+            pos_last = pos_first + nrows - 1
+            nblk = 0 if pos_last < 0 else min(pos_last // 128 + 1, bt_cols)
+            perm = [i if i < nrows else -1 for i in range(32)]
+            if nrows > 2 and nblk > 0:
+                sig = [0] * nrows
+                for i in range(nrows):
+                    pos = pos_first + i
+                    for b in wl.topk[t0 + i]:
+                        b = int(b)
+                        if pos >= 0 and 0 <= b < nblk and b <= pos // 128:
+                            sig[i] |= 1 << (b & 63)
+                left, perm, p = list(range(nrows)), [-1] * 32, 0
+                while left:
+                    a, b = left.pop(0), -1
+                    if left:
+                        b = max(left, key=lambda j: (6 * bin(sig[a] & sig[j]).count("1") + 64
+                                                     - bin(sig[j]).count("1"), -j))
+                        left.remove(b)
+                    perm[2 * p], perm[2 * p + 1], p = a, b, p + 1
+            orders.append(perm)
+    return np.array(orders, dtype=np.int8).reshape(-1, 32)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k=4, qlens=[70, 200, 33], context=[3000, 1500, 0], seed=80),                    # 8 per kv head
+    dict(kv_dtype="fp8", k=3, qlens=[64, 130], context=[4000, 2500], seed=81),
+    dict(Hq=12, Hkv=2, kv_dtype="nvfp4", k=5, qlens=[100, 40], context=[2600, 3100], seed=82),   # 6: spare columns
+    dict(Hq=7, Hkv=1, k=2, qlens=[1, 2, 3, 45, 300], context=[0, 5, 700, 0, 2000], seed=83),     # 7, tiny requests
+])
+def test_prefill_row_pairing(kw):
+    # At 6 to 8 query heads per kv head the prefill first pairs each query
+    # tile's rows by their selections (one 32-byte row order per tile in the
+    # workspace).  The orders must be exactly the pairing rule's, and every
+    # row must match the oracle with the whole workspace, half of it (the
+    # later tiles keep their natural order) and none.
+    wl = make_workload("C4s", **kw)
+    cache = make_kv_cache(wl, DEV)
+    want = _expected_row_orders(wl)
+    n_tiles = want.shape[0]
+    full = msa.msa_prefill_workspace_size(wl.total_q, wl.num_q_heads, wl.head_dim, wl.topk_k)
+    assert full >= 32 * n_tiles
+    outs = []
+    for nbytes in (full, 32 * (n_tiles // 2), 1):
+        ws = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
+        out, _ = _parity(wl, cache=cache, workspace=ws)
+        outs.append(out)
+        if nbytes == full:
+            got = ws[:32 * n_tiles].cpu().view(torch.int8).numpy().reshape(-1, 32)
+            bad = np.nonzero((got != want).any(1))[0]
+            assert bad.size == 0, f"tile {bad[0]}: {got[bad[0]].tolist()} against {want[bad[0]].tolist()}"
+            assert ((want != np.arange(32)) & (want >= 0)).any(), "no tile was reordered"
+    # same rows, other tile groupings: equal up to rounding
+    assert (outs[0].float() - outs[2].float()).abs().max().item() < 2 * ATOL
 
 
 def test_decode_deterministic():
