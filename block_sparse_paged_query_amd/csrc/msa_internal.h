@@ -54,8 +54,9 @@ struct AttendArgs {
   float* ws_o;    // [rows][Hq][nsplit][D]
   float* ws_ml;   // [rows][Hq][nsplit][2]
   int32_t num_cus;   // compute units of the device (launch shaping)
-  // Prefill at 6-8 query heads per kv head: 32 bytes of row order per query
-  // tile for perm_cap tiles (device workspace), or NULL to keep row order.
+  // Prefill at 4-8 query heads per kv head: device workspace of perm_cap x
+  // 32 bytes for the row order of each query tile (QT bytes a tile), or NULL
+  // to keep the natural order.
   int8_t* row_perm;
   int32_t perm_cap;
 };

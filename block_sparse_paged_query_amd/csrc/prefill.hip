@@ -39,9 +39,9 @@
 // are skipped.  Online softmax state stays in registers; the workgroup
 // writes its rows' bf16 outputs at the end.
 // Workgroups of one kv head share an XCD (blockIdx % Hkv), so K/V blocks
-// re-read by neighbouring query tiles hit that XCD's L2.  At 6 to 8 query
-// heads per kv head a tile holds two rows, and a small kernel run first
-// (pf_pair_kernel) pairs each query tile's rows with alike selections, so
+// re-read by neighbouring query tiles hit that XCD's L2.  At 4 to 8 query
+// heads per kv head a tile holds 2 to 4 rows, and a small kernel run first
+// (pf_pair_kernel) groups each query tile's rows with alike selections, so
 // that fewer tiles are active per block.
 //
 // fp8 and NVFP4 pages ([FI] forward folds the fp8 scales; [NV4] customize_spec
@@ -615,74 +615,100 @@ __device__ __forceinline__ PfTile pf_find_tile(const AttendArgs& a, int t, int Q
   return tl;
 }
 
-// ---- row pairing for two-row tiles ---------------------------------------
+// ---- row grouping for tiles of 2 to 4 rows -------------------------------
 //
-// At 6 to 8 query heads per kv head a matrix tile holds two query rows, and
-// it runs a block's products when either row selected the block.  Rows whose
-// selections overlap therefore share tiles: one wave per 32-row query tile
-// pairs its rows greedily, the lowest unpaired row taking the unpaired row
-// with the highest 6 |common blocks| - |its blocks| (the lowest such row on
-// ties), each row's selected blocks folded to 64 bits.  Pair p goes to wave
-// p of the prefill workgroup.  Any order gives the same results up to
-// rounding (a row's softmax state is its own); this only orders the work.
-// On C4's independent draws it cuts the active (tile, block) pairs by 7 %.
+// At 4 to 8 query heads per kv head a matrix tile holds RT = 2 to 4 query
+// rows (QT = 16 RT per workgroup), and it runs a block's products when any
+// of its rows selected the block.  Rows whose selections overlap therefore
+// share tiles: one wave per query tile groups its rows greedily.  The lowest
+// ungrouped row opens a group; the group then takes, RT - 1 times, the
+// ungrouped row with the highest 6 |common blocks| - |its blocks| against the
+// blocks the group holds so far (the lowest such row on ties), each row's
+// selected blocks folded to 64 bits.  Each finished group goes to the SIMD
+// (waves s, s + 4, s + 8, s + 12 share one) whose groups so far share the
+// fewest blocks with it, counted per block with multiplicity, so that a
+// block's products spread over the four SIMDs; the group takes that SIMD's
+// next free wave.  Any order gives the same results up to rounding (a row's
+// softmax state is its own); this only orders the work.  On C4's
+// independent draws the pairs cut the active (tile, block) pairs by 7 % and
+// the busiest SIMD's share of a block by 7 %.
+constexpr bool pf_groups_rows(int RT) { return RT >= 2 && RT <= 4; }
 
-// perm[2 p + k] = row k of pair p (k = 1 is -1 for a lone last row).
-__device__ __forceinline__ void pf_pair_rows(const uint32_t (*sig_w)[2], int8_t* perm, int nrows) {
+// perm[RT w + k] = row k of the group on wave w, or -1.
+__device__ __forceinline__ void pf_group_rows(const uint32_t (*sig_w)[2], int8_t* perm, int nrows, int RT) {
   const int lane = threadIdx.x & 63;
   const bool mine = lane < nrows;
   const uint32_t lo = mine ? sig_w[lane][0] : 0u, hi = mine ? sig_w[lane][1] : 0u;
   const uint64_t sig = ((uint64_t)hi << 32) | lo;
   const int base = 64 - __popcll(sig);   // scores 6 common + 64 - own count lie in [0, 448]
-  uint64_t U = __ballot(mine);           // unpaired rows
-  int np = 0;
+  uint64_t U = __ballot(mine);           // rows not yet in a group
+  // lane q < 4 keeps SIMD q's per-block tile counts (0 to 4) as three bit planes
+  uint64_t P0 = 0, P1 = 0, P2 = 0;
+  int cap = 0;
+  perm[lane] = (int8_t)-1;
   while (U) {
-    const int ra = __ffsll((unsigned long long)U) - 1;
+    int rows[4] = {__ffsll((unsigned long long)U) - 1, -1, -1, -1};
     U &= U - 1;
-    int rb = -1;
-    if (U) {
-      const uint64_t sa = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, ra) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane(lo, ra);
-      const int sc = 6 * __popcll(sa & sig) + base;
+    uint64_t act = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, rows[0]) << 32) |
+                   (uint32_t)__builtin_amdgcn_readlane(lo, rows[0]);
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      if (k >= RT || !U) break;
+      const int sc = 6 * __popcll(act & sig) + base;
       uint64_t C = U;   // the best candidates so far, narrowed one score bit at a time
 #pragma unroll
-      for (int k = 8; k >= 0; --k) {
-        const uint64_t B = __ballot((sc >> k) & 1) & C;
+      for (int b = 8; b >= 0; --b) {
+        const uint64_t B = __ballot((sc >> b) & 1) & C;
         if (B) C = B;
       }
-      rb = __ffsll((unsigned long long)C) - 1;
-      U &= ~(1ull << rb);
+      rows[k] = __ffsll((unsigned long long)C) - 1;
+      U &= ~(1ull << rows[k]);
+      act |= ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, rows[k]) << 32) |
+             (uint32_t)__builtin_amdgcn_readlane(lo, rows[k]);
+    }
+    const int d = __popcll(P0 & act) + 2 * __popcll(P1 & act) + 4 * __popcll(P2 & act);
+    const int key = lane < 4 && cap < 4 ? (d << 2) | lane : 0x7fffffff;
+    const int best = min(min(__builtin_amdgcn_readlane(key, 0), __builtin_amdgcn_readlane(key, 1)),
+                         min(__builtin_amdgcn_readlane(key, 2), __builtin_amdgcn_readlane(key, 3))) & 3;
+    const int wv = best + 4 * __builtin_amdgcn_readlane(cap, best);
+    if (lane == best) {
+      const uint64_t c0 = P0 & act, c1 = P1 & c0;
+      P0 ^= act;
+      P1 ^= c0;
+      P2 |= c1;
+      ++cap;
     }
     if (lane == 0) {
-      perm[2 * np] = (int8_t)ra;
-      perm[2 * np + 1] = (int8_t)rb;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < RT) perm[RT * wv + k] = (int8_t)rows[k];
     }
-    ++np;
   }
 }
 
 // One workgroup per query tile t (the prefill kernel's numbering): its 512
-// threads read the tile's top-k rows (one element each at 32 x 16), wave 0
-// pairs the rows and writes the tile's 32-slot row order to perm_out[32 t ..]
-// for every real tile below cap (padding tiles have no order).
+// threads read the tile's top-k rows, wave 0 groups the rows and writes the
+// tile's QT-slot row order to perm_out[QT t ..] for every real tile below cap
+// (padding tiles have no order).
 constexpr int kPairThreads = 512;
 
 __global__ __launch_bounds__(kPairThreads) void pf_pair_kernel(const AttendArgs a, int8_t* perm_out, int cap) {
-  __shared__ uint32_t s_sig[32][2];
-  __shared__ int8_t s_perm[32];
+  __shared__ uint32_t s_sig[64][2];
+  __shared__ int8_t s_perm[64];
   __shared__ int s_tile[4];
+  const int RT = 16 / a.group, QT = kPfWaves * kPfTiles * RT;
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   if (t >= cap) return;
   if (tid < 64) {
-    const PfTile tl = pf_find_tile(a, t, kPfWaves * kPfTiles * 2, lane);
+    const PfTile tl = pf_find_tile(a, t, QT, lane);
     if (tid == 0) {
       s_tile[0] = tl.mode;
       s_tile[1] = tl.req;
       s_tile[2] = tl.row0;
       s_tile[3] = tl.row_end;
     }
-    s_sig[lane >> 1][lane & 1] = 0u;
   }
+  if (tid < 128) s_sig[tid >> 1][tid & 1] = 0u;
   __syncthreads();
   const int mode = s_tile[0], req = s_tile[1], row0 = s_tile[2], row_end = s_tile[3];
   if (mode != 0 || row0 >= row_end) return;
@@ -691,8 +717,8 @@ __global__ __launch_bounds__(kPairThreads) void pf_pair_kernel(const AttendArgs 
   const int pos_first = a.seq_lens[req] - (cu1 - cu0) + (row0 - cu0);
   const int pos_last = pos_first + nrows - 1;
   const int nblk = pos_last < 0 ? 0 : min(pos_last / kBlockTokens + 1, a.bt_cols);
-  const bool pair = nrows > 2 && nblk > 0;
-  if (pair) {
+  const bool group = nrows > 2 && nblk > 0;
+  if (group) {
     for (int idx = tid; idx < nrows * a.topk_k; idx += kPairThreads) {
       const int rr = idx / a.topk_k, tk = idx - rr * a.topk_k;
       const int pos = pos_first + rr;
@@ -703,9 +729,12 @@ __global__ __launch_bounds__(kPairThreads) void pf_pair_kernel(const AttendArgs 
     __syncthreads();
   }
   if (tid >= 64) return;
-  if (lane < 32) s_perm[lane] = (int8_t)(lane < nrows ? lane : -1);
-  if (pair) pf_pair_rows(s_sig, s_perm, nrows);
-  if (lane < 32) perm_out[(int64_t)t * 32 + lane] = s_perm[lane];
+  if (group) {
+    pf_group_rows(s_sig, s_perm, nrows, RT);
+  } else {
+    s_perm[lane] = (int8_t)(lane < nrows ? lane : -1);
+  }
+  if (lane < QT) perm_out[(int64_t)t * QT + lane] = s_perm[lane];
 }
 
 template <int FMT, int D, int MW>
@@ -729,8 +758,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   __shared__ uint16_t s_list[WIN];            // selected blocks of the window, ascending
   __shared__ int32_t s_phys[WIN];             // their physical block ids
   __shared__ int s_info[4];
-  __shared__ int8_t s_perm[32];               // two-row tiles: tile slot -> row
-  __shared__ int8_t s_slot[32];               // two-row tiles: row -> tile slot
+  __shared__ int8_t s_perm[64];               // tiles of 2-4 rows: tile slot -> row
+  __shared__ int8_t s_slot[64];               // tiles of 2-4 rows: row -> tile slot
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int G = a.group, RT = 16 / G, QT = kPfWaves * kPfTiles * RT;
@@ -739,9 +768,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
 
   // ---- which rows: a tile of one request, padding rows, or nothing.  The
   // tile's row order (two-row tiles) is read meanwhile, if there is one.
-  const bool have_perm = RT == 2 && a.row_perm != nullptr && t < a.perm_cap;
+  const bool grouped = pf_groups_rows(RT);
+  const bool have_perm = grouped && a.row_perm != nullptr && t < a.perm_cap;
   int perm_v = -1;
-  if (have_perm && wave == 1 && lane < 32) perm_v = a.row_perm[(int64_t)t * 32 + lane];
+  if (have_perm && wave == 1 && lane < QT) perm_v = a.row_perm[(int64_t)t * QT + lane];
   if (wave == 0) {
     const PfTile tl = pf_find_tile(a, t, QT, lane);
     if (lane == 0) {
@@ -773,10 +803,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   const int nblk = pos_last < 0 ? 0 : min(pos_last / kBlockTokens + 1, a.bt_cols);
   const int32_t* bt_row = a.block_table + (int64_t)req * a.bt_stride;
   const int nrows = row_end - row0;
-  // two-row tiles: slot k of wave w holds row s_perm[2 w + k] (the order
-  // pf_pair_kernel chose, else the natural one); s_slot is the inverse
-  if (RT == 2) {
-    if (wave == 1 && lane < 32) {
+  // tiles of 2-4 rows: slot k of wave w holds row s_perm[RT w + k] (the
+  // order pf_pair_kernel chose, else the natural one); s_slot is the inverse
+  if (grouped) {
+    if (wave == 1 && lane < QT) {
       int p = have_perm ? perm_v : lane;
       if (p < 0 || p >= nrows) p = -1;
       s_perm[lane] = (int8_t)p;
@@ -788,14 +818,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
 
   // ---- this wave's query operands and row data.  The wave's tile slots are
   // bits [wbit0, wbit0 + RT) of a block's mask; slot k holds row wbit0 + k,
-  // or at RT = 2 row s_perm[wbit0 + k].
+  // or, in tiles of 2-4 rows, row s_perm[wbit0 + k].
   PfWave<OT, D> w;
   const int wbit0 = wave * kPfTiles * RT;
 #pragma unroll
   for (int i = 0; i < kPfTiles; ++i) {
     const int slot = (wave * kPfTiles + i) * RT + r / G;
     int rr = slot < nrows ? slot : -1;
-    if (RT == 2) rr = s_perm[slot & 31];
+    if (grouped) rr = s_perm[slot & 63];
     const bool ok = r < RT * G && rr >= 0;
     w.lrow[i] = ok ? rr : -1;
     w.lbit[i] = slot - wbit0;
@@ -841,7 +871,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
       const int blk = a.topk[(int64_t)(row0 + rr) * a.topk_stride + tk];
       if (pos >= 0 && blk >= w0 && blk < w1 && blk <= pos / kBlockTokens)
       {
-        const int sl = RT == 2 ? (int)s_slot[rr] : rr;
+        const int sl = grouped ? (int)s_slot[rr] : rr;
         if (sl >= 0) atomicOr(&s_mask[blk - w0][sl >> 5], 1u << (sl & 31));
       }
     }
@@ -1131,15 +1161,22 @@ static hipError_t launch_pf(const AttendArgs& a, dim3 grid, int n_slots, hipStre
 }
 
 hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t stream) {
-  const int QT = kPfWaves * kPfTiles * (16 / a.group);
+  const int RT = 16 / a.group, QT = kPfWaves * kPfTiles * RT;
   // tiles: ceil(rows / QT) per request and per padding range (before the
   // first request, after the last) is at most ceil(total / QT) + R + 2
   const int n_slots = (a.total_rows + QT - 1) / QT + a.num_reqs + 2;
   const dim3 grid((unsigned)((int64_t)n_slots * a.num_kv_heads));
-  if (a.row_perm != nullptr && 16 / a.group == 2) {
-    const int n_pair = min(n_slots, a.perm_cap);
-    log_launch("pf_pair_kernel: %d query tiles of 32 rows", n_pair);
-    hipLaunchKernelGGL(pf_pair_kernel, dim3((unsigned)n_pair), dim3(kPairThreads), 0, stream, a, a.row_perm, n_pair);
+  // the caller's workspace (perm_cap units of 32 bytes) holds QT bytes of row
+  // order per query tile; from here on perm_cap counts tiles
+  AttendArgs ag = a;
+  if (!pf_groups_rows(RT) || ag.row_perm == nullptr || (int64_t)ag.perm_cap * 32 < QT) {
+    ag.row_perm = nullptr;
+    ag.perm_cap = 0;
+  } else {
+    ag.perm_cap = (int32_t)((int64_t)ag.perm_cap * 32 / QT);
+    const int n_pair = min(n_slots, ag.perm_cap);
+    log_launch("pf_pair_kernel: %d query tiles of %d rows in groups of %d", n_pair, QT, RT);
+    hipLaunchKernelGGL(pf_pair_kernel, dim3((unsigned)n_pair), dim3(kPairThreads), 0, stream, ag, ag.row_perm, n_pair);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1147,12 +1184,12 @@ hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t strea
              "heads, 16 waves each", fmt == kFmtBf16 ? "bf16" : (fmt == kFmtFp8 ? "fp8" : "nvfp4"), a.head_dim,
              a.group, n_slots, QT, a.num_kv_heads);
   if (a.head_dim == 128) {
-    if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 128>(a, grid, n_slots, stream);
-    if (fmt == kFmtFp8) return launch_pf<kFmtFp8, 128>(a, grid, n_slots, stream);
-    return launch_pf<kFmtNvfp4, 128>(a, grid, n_slots, stream);
+    if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 128>(ag, grid, n_slots, stream);
+    if (fmt == kFmtFp8) return launch_pf<kFmtFp8, 128>(ag, grid, n_slots, stream);
+    return launch_pf<kFmtNvfp4, 128>(ag, grid, n_slots, stream);
   }
-  if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 64>(a, grid, n_slots, stream);
-  return launch_pf<kFmtFp8, 64>(a, grid, n_slots, stream);
+  if (fmt == kFmtBf16) return launch_pf<kFmtBf16, 64>(ag, grid, n_slots, stream);
+  return launch_pf<kFmtFp8, 64>(ag, grid, n_slots, stream);
 }
 
 }  // namespace msa

@@ -252,10 +252,13 @@ MSA_API msa_status_t msa_sparse_decode_noalloc(
 MSA_API size_t msa_decode_noalloc_scratch_bytes(void);
 
 /*
- * Bytes of workspace msa_sparse_prefill can use: 32 per 32-row query tile,
- * sized for any split of total_q rows into requests (32 * (total_q +
- * ceil(total_q / 32)); 0 for total_q <= 0).  The other arguments are
- * accepted for symmetry with msa_decode_workspace_size and not used.
+ * Bytes of workspace msa_sparse_prefill can use: 32 * (total_q +
+ * ceil(total_q / 32)), 0 for total_q <= 0.  A query tile's row order takes
+ * as many bytes as the tile has rows (32, 48 or 64), so this covers every
+ * tile of any split of total_q rows into requests at 6 to 8 query heads per
+ * kv head, and every tile of splits with at most about half as many
+ * requests as rows at 4 or 5.  The other arguments are accepted for
+ * symmetry with msa_decode_workspace_size and not used.
  */
 MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
                                           int32_t topk_k);
@@ -278,11 +281,11 @@ MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, 
  * fp16).
  *
  * workspace: device memory the call may overwrite (no alignment needed), or
- * NULL.  At 6 to 8 query heads per kv head the call first writes one 32-byte
- * row order per query tile there (rows with alike top-k rows share matrix
- * tiles, which saves products); tiles past workspace_bytes / 32 keep their
- * natural order.  Any size gives the same results up to rounding; the
- * output does not depend on what the workspace held before the call.
+ * NULL.  At 4 to 8 query heads per kv head the call first writes one row
+ * order per query tile there (rows with alike top-k rows share matrix
+ * tiles, which saves products); tiles past what workspace_bytes holds keep
+ * their natural order.  Any size gives the same results up to rounding;
+ * the output does not depend on what the workspace held before the call.
  */
 MSA_API msa_status_t msa_sparse_prefill(
     const void* q, int32_t q_dtype, int32_t total_q, int32_t num_q_heads,

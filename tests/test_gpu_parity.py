@@ -522,22 +522,30 @@ def test_decode_split_counts(name):
 
 
 def _expected_row_orders(wl):
-    # The prefill's row pairing for two-row tiles, restated: per 32-row query
-    # tile (requests in order), each row's selected blocks that it may see
-    # (below the tile's block count), folded to 64 bits; the lowest unpaired
-    # row takes the unpaired row with the highest 6 |common| + 64 - |own|
-    # (the lowest on ties); pair p fills slots 2p and 2p + 1.  Tiles of at
-    # most two rows, or with no blocks, keep the natural order.
+    # The prefill's row grouping for tiles of RT = 2 to 4 rows (4 to 8 query
+    # heads per kv head), restated.  Per QT = 16 RT-row query tile (requests
+    # in order): each row's visible selected blocks below the tile's block
+    # count, folded to 64 bits.  The lowest ungrouped row opens a group, which
+    # then takes RT - 1 times the ungrouped row with the highest
+    # 6 |common with the group| + 64 - |own| (the lowest on ties).  A finished
+    # group goes to the SIMD q (waves q, q + 4, q + 8, q + 12) with fewer than
+    # 4 groups whose per-block group counts, summed over the group's blocks,
+    # are lowest (the lowest q on ties), on that SIMD's next wave; slots
+    # RT w .. RT w + RT - 1 of wave w hold its rows.  Tiles of at most two
+    # rows, or with no blocks, keep the natural order.
+    G = wl.num_q_heads // wl.num_kv_heads
+    RT = 16 // G
+    QT = 16 * RT
     orders = []
     cu, seq, bt_cols = wl.cu_seqlens_q, wl.seq_lens, wl.block_table.shape[1]
     for r in range(len(seq)):
         ctx0 = int(seq[r]) - int(cu[r + 1] - cu[r])
-        for t0 in range(int(cu[r]), int(cu[r + 1]), 32):
-            nrows = min(32, int(cu[r + 1]) - t0)
+        for t0 in range(int(cu[r]), int(cu[r + 1]), QT):
+            nrows = min(QT, int(cu[r + 1]) - t0)
             pos_first = ctx0 + t0 - int(cu[r])
             pos_last = pos_first + nrows - 1
             nblk = 0 if pos_last < 0 else min(pos_last // 128 + 1, bt_cols)
-            perm = [i if i < nrows else -1 for i in range(32)]
+            perm = [i if i < nrows else -1 for i in range(QT)]
             if nrows > 2 and nblk > 0:
                 sig = [0] * nrows
                 for i in range(nrows):
@@ -546,16 +554,27 @@ def _expected_row_orders(wl):
                         b = int(b)
                         if pos >= 0 and 0 <= b < nblk and b <= pos // 128:
                             sig[i] |= 1 << (b & 63)
-                left, perm, p = list(range(nrows)), [-1] * 32, 0
+                ones = lambda x: bin(x).count("1")
+                left, perm = list(range(nrows)), [-1] * QT
+                load, cap = [[0] * 64 for _ in range(4)], [0] * 4
                 while left:
-                    a, b = left.pop(0), -1
-                    if left:
-                        b = max(left, key=lambda j: (6 * bin(sig[a] & sig[j]).count("1") + 64
-                                                     - bin(sig[j]).count("1"), -j))
+                    group = [left.pop(0)]
+                    u = sig[group[0]]
+                    while len(group) < RT and left:
+                        b = max(left, key=lambda j: (6 * ones(u & sig[j]) + 64 - ones(sig[j]), -j))
                         left.remove(b)
-                    perm[2 * p], perm[2 * p + 1], p = a, b, p + 1
+                        group.append(b)
+                        u |= sig[b]
+                    bits = [k for k in range(64) if u >> k & 1]
+                    q = min((sum(load[q][k] for k in bits), q) for q in range(4) if cap[q] < 4)[1]
+                    wv = q + 4 * cap[q]
+                    cap[q] += 1
+                    for k in bits:
+                        load[q][k] += 1
+                    for k, row in enumerate(group):
+                        perm[RT * wv + k] = row
             orders.append(perm)
-    return np.array(orders, dtype=np.int8).reshape(-1, 32)
+    return np.array(orders, dtype=np.int8).reshape(-1, QT)
 
 
 @pytest.mark.parametrize("kw", [
@@ -563,29 +582,31 @@ def _expected_row_orders(wl):
     dict(kv_dtype="fp8", k=3, qlens=[64, 130], context=[4000, 2500], seed=81),
     dict(Hq=12, Hkv=2, kv_dtype="nvfp4", k=5, qlens=[100, 40], context=[2600, 3100], seed=82),   # 6: spare columns
     dict(Hq=7, Hkv=1, k=2, qlens=[1, 2, 3, 45, 300], context=[0, 5, 700, 0, 2000], seed=83),     # 7, tiny requests
+    dict(Hq=16, Hkv=4, k=4, qlens=[150, 200, 7], context=[3000, 1500, 900], seed=84),    # 4: groups of 4 rows
+    dict(Hq=10, Hkv=2, kv_dtype="fp8", k=3, qlens=[130, 60], context=[2500, 3500], seed=85),     # 5: groups of 3
 ])
-def test_prefill_row_pairing(kw):
-    # At 6 to 8 query heads per kv head the prefill first pairs each query
-    # tile's rows by their selections (one 32-byte row order per tile in the
-    # workspace).  The orders must be exactly the pairing rule's, and every
+def test_prefill_row_grouping(kw):
+    # At 4 to 8 query heads per kv head the prefill first groups each query
+    # tile's rows by their selections (one QT-byte row order per tile in the
+    # workspace).  The orders must be exactly the grouping rule's, and every
     # row must match the oracle with the whole workspace, half of it (the
     # later tiles keep their natural order) and none.
     wl = make_workload("C4s", **kw)
     cache = make_kv_cache(wl, DEV)
     want = _expected_row_orders(wl)
-    n_tiles = want.shape[0]
+    n_tiles, qt = want.shape
     full = msa.msa_prefill_workspace_size(wl.total_q, wl.num_q_heads, wl.head_dim, wl.topk_k)
-    assert full >= 32 * n_tiles
+    assert full >= qt * n_tiles
     outs = []
-    for nbytes in (full, 32 * (n_tiles // 2), 1):
-        ws = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
+    for nbytes in (full, qt * (n_tiles // 2), 1):
+        ws = torch.full((max(nbytes, 1),), 0x55, dtype=torch.uint8, device=DEV)
         out, _ = _parity(wl, cache=cache, workspace=ws)
         outs.append(out)
         if nbytes == full:
-            got = ws[:32 * n_tiles].cpu().view(torch.int8).numpy().reshape(-1, 32)
+            got = ws[:qt * n_tiles].cpu().view(torch.int8).numpy().reshape(-1, qt)
             bad = np.nonzero((got != want).any(1))[0]
             assert bad.size == 0, f"tile {bad[0]}: {got[bad[0]].tolist()} against {want[bad[0]].tolist()}"
-            assert ((want != np.arange(32)) & (want >= 0)).any(), "no tile was reordered"
+            assert ((want != np.arange(qt)) & (want >= 0)).any(), "no tile was reordered"
     # same rows, other tile groupings: equal up to rounding
     assert (outs[0].float() - outs[2].float()).abs().max().item() < 2 * ATOL
 
@@ -732,6 +753,7 @@ def test_launch_log(capfd, monkeypatch):
     # C2s: 3 rows x 8 kv heads, split so that the machine fills, then merged
     assert "[msa] attend_rows_kernel decode, bf16 pages, head_dim 128:" in err, err
     assert "[msa] attend_merge_kernel head_dim 128: 192 (row, head) pairs" in err, err
+    assert "[msa] pf_pair_kernel: " in err and "query tiles of 64 rows in groups of 4" in err, err
     assert "[msa] prefill_blocks_kernel bf16 pages, head_dim 128, 4 query heads per kv head" in err, err
     monkeypatch.setenv("MSA_LOG", "0")
     for wl, cache, q in runs:
