@@ -329,7 +329,7 @@ def main():
             and args.selection == "independent" and not args.heads
         args.also = "C3,C4,C5" if default_main else ""
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -55,7 +55,7 @@ extern "C" {
 typedef enum msa_status {
   MSA_OK = 0,
   MSA_ERR_INVALID_ARGUMENT = 1,   /* a value a caller must fix ([SPA] ValueError / assertion) */
-  MSA_ERR_UNSUPPORTED = 2,        /* a valid shape / dtype this build does not serve */
+  MSA_ERR_UNSUPPORTED = 2,        /* a valid shape / dtype the library does not serve */
   MSA_ERR_WORKSPACE_TOO_SMALL = 3,
   MSA_ERR_HIP = 4                 /* a HIP launch failed; see msa_last_error() */
 } msa_status_t;
