@@ -313,6 +313,13 @@ def test_prefill_parity_full_size(kv_dtype, selection, every_row):
     _parity(wl, None if every_row else _c4_stratified_rows(wl))
 
 
+def test_prefill_parity_full_size_four_heads_per_kv_head():
+    # C4's rows and selections at 32 query / 8 kv heads: 64-row query tiles
+    # whose rows the grouping kernel puts four to a matrix tile
+    wl = make_workload("C4", Hq=32, Hkv=8)
+    _parity(wl, _c4_stratified_rows(wl))
+
+
 @pytest.mark.parametrize("name,cols", [("C4s", 2050), ("C4s:fp8", 2050), ("C2s", 4100)])
 def test_wide_block_table(name, cols):
     # a block table wider than one block window of the matrix-core prefill
