@@ -41,7 +41,7 @@
 // Workgroups of one kv head share an XCD (blockIdx % Hkv), so K/V blocks
 // re-read by neighbouring query tiles hit that XCD's L2.  At 4 to 8 query
 // heads per kv head a tile holds 2 to 4 rows, and a small kernel run first
-// (pf_pair_kernel) groups each query tile's rows with alike selections, so
+// (pf_group_kernel) groups each query tile's rows with alike selections, so
 // that fewer tiles are active per block.
 //
 // fp8 and NVFP4 pages ([FI] forward folds the fp8 scales; [NV4] customize_spec
@@ -690,9 +690,9 @@ __device__ __forceinline__ void pf_group_rows(const uint32_t (*sig_w)[2], int8_t
 // threads read the tile's top-k rows, wave 0 groups the rows and writes the
 // tile's QT-slot row order to perm_out[QT t ..] for every real tile below cap
 // (padding tiles have no order).
-constexpr int kPairThreads = 512;
+constexpr int kGroupThreads = 512;
 
-__global__ __launch_bounds__(kPairThreads) void pf_pair_kernel(const AttendArgs a, int8_t* perm_out, int cap) {
+__global__ __launch_bounds__(kGroupThreads) void pf_group_kernel(const AttendArgs a, int8_t* perm_out, int cap) {
   __shared__ uint32_t s_sig[64][2];
   __shared__ int8_t s_perm[64];
   __shared__ int s_tile[4];
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kPairThreads) void pf_pair_kernel(const AttendArgs 
   const int nblk = pos_last < 0 ? 0 : min(pos_last / kBlockTokens + 1, a.bt_cols);
   const bool group = nrows > 2 && nblk > 0;
   if (group) {
-    for (int idx = tid; idx < nrows * a.topk_k; idx += kPairThreads) {
+    for (int idx = tid; idx < nrows * a.topk_k; idx += kGroupThreads) {
       const int rr = idx / a.topk_k, tk = idx - rr * a.topk_k;
       const int pos = pos_first + rr;
       const int blk = a.topk[(int64_t)(row0 + rr) * a.topk_stride + tk];
@@ -804,7 +804,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_blocks_kernel(const Attend
   const int32_t* bt_row = a.block_table + (int64_t)req * a.bt_stride;
   const int nrows = row_end - row0;
   // tiles of 2-4 rows: slot k of wave w holds row s_perm[RT w + k] (the
-  // order pf_pair_kernel chose, else the natural one); s_slot is the inverse
+  // order pf_group_kernel chose, else the natural one); s_slot is the inverse
   if (grouped) {
     if (wave == 1 && lane < QT) {
       int p = have_perm ? perm_v : lane;
@@ -1174,9 +1174,9 @@ hipError_t launch_prefill_blocks(const AttendArgs& a, int fmt, hipStream_t strea
     ag.perm_cap = 0;
   } else {
     ag.perm_cap = (int32_t)((int64_t)ag.perm_cap * 32 / QT);
-    const int n_pair = min(n_slots, ag.perm_cap);
-    log_launch("pf_pair_kernel: %d query tiles of %d rows in groups of %d", n_pair, QT, RT);
-    hipLaunchKernelGGL(pf_pair_kernel, dim3((unsigned)n_pair), dim3(kPairThreads), 0, stream, ag, ag.row_perm, n_pair);
+    const int n_group = min(n_slots, ag.perm_cap);
+    log_launch("pf_group_kernel: %d query tiles of %d rows in groups of %d", n_group, QT, RT);
+    hipLaunchKernelGGL(pf_group_kernel, dim3((unsigned)n_group), dim3(kGroupThreads), 0, stream, ag, ag.row_perm, n_group);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -760,7 +760,7 @@ def test_launch_log(capfd, monkeypatch):
     # C2s: 3 rows x 8 kv heads, split so that the machine fills, then merged
     assert "[msa] attend_rows_kernel decode, bf16 pages, head_dim 128:" in err, err
     assert "[msa] attend_merge_kernel head_dim 128: 192 (row, head) pairs" in err, err
-    assert "[msa] pf_pair_kernel: " in err and "query tiles of 64 rows in groups of 4" in err, err
+    assert "[msa] pf_group_kernel: " in err and "query tiles of 64 rows in groups of 4" in err, err
     assert "[msa] prefill_blocks_kernel bf16 pages, head_dim 128, 4 query heads per kv head" in err, err
     monkeypatch.setenv("MSA_LOG", "0")
     for wl, cache, q in runs:
