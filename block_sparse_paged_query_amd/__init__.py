@@ -254,6 +254,24 @@ def msa_prefill_workspace_size(total_q, num_q_heads, head_dim, topk_k):
     return load_library().msa_prefill_workspace_size(total_q, num_q_heads, head_dim, topk_k)
 
 
+def _check_workspace(ws):
+    # the library writes workspace_bytes bytes from the pointer on, on the GPU
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.device.type != "cuda":
+        raise ValueError(f"workspace must be a GPU tensor, got {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def _ws_args(ws, device):
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
 def _check_q(q, name="q"):
     _need(q, name, torch.bfloat16, 3)
     if q.device.type != "cuda":
@@ -265,6 +283,7 @@ def _check_q(q, name="q"):
 def msa_sparse_decode(q, kv: KVCache, topk, block_table, seq_lens, softmax_scale, *, decode_query_len=1,
                       out=None, workspace=None):
     """Block-sparse GQA decode; q/out [batch * decode_query_len, Hq, D] bf16."""
+    _check_workspace(workspace)
     if topk.dim() == 3:
         topk = topk[0]
     _need_table_rows(block_table, seq_lens.shape[0], "block_table")
@@ -290,11 +309,11 @@ def msa_sparse_decode(q, kv: KVCache, topk, block_table, seq_lens, softmax_scale
     if workspace is None:
         nbytes = msa_decode_workspace_size(rows, hq, d, topk.shape[1])
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _ws_args(workspace, dev)
     kvs = kv._struct()
     _call("msa_sparse_decode", _ptr(q), MSA_BF16, num_reqs, decode_query_len, hq, ctypes.byref(kvs),
           _ptr(topk), topk.stride(0), topk.shape[1], _ptr(block_table), block_table.stride(0),
-          block_table.shape[1], _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(workspace),
-          workspace.numel() * workspace.element_size(), _stream(dev))
+          block_table.shape[1], _ptr(seq_lens), float(softmax_scale), _ptr(out), ws_ptr, ws_bytes, _stream(dev))
     return out
 
 
@@ -333,6 +352,7 @@ def msa_sparse_decode_noalloc(q, kv: KVCache, topk, block_table, seq_lens, softm
 def msa_sparse_prefill(q, kv: KVCache, topk, block_table, cu_seqlens_q, seq_lens, softmax_scale, *, out=None,
                        workspace=None):
     """Block-sparse ragged causal prefill; q/out [total_q, Hq, D] bf16 (padded rows -> 0)."""
+    _check_workspace(workspace)
     if topk.dim() == 3:
         topk = topk[0]
     _need_table_rows(block_table, seq_lens.shape[0], "block_table")
@@ -353,11 +373,11 @@ def msa_sparse_prefill(q, kv: KVCache, topk, block_table, cu_seqlens_q, seq_lens
     if workspace is None:
         nbytes = msa_prefill_workspace_size(total_q, hq, d, topk.shape[1])
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _ws_args(workspace, dev)
     kvs = kv._struct()
     _call("msa_sparse_prefill", _ptr(q), MSA_BF16, total_q, hq, ctypes.byref(kvs), _ptr(topk), topk.stride(0),
           topk.shape[1], _ptr(block_table), block_table.stride(0), block_table.shape[1], seq_lens.shape[0],
-          _ptr(cu_seqlens_q), _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(workspace),
-          workspace.numel() * workspace.element_size(), _stream(dev))
+          _ptr(cu_seqlens_q), _ptr(seq_lens), float(softmax_scale), _ptr(out), ws_ptr, ws_bytes, _stream(dev))
     return out
 
 
@@ -371,6 +391,7 @@ def msa_sparse_attention(q, kv: KVCache, topk, num_decode_tokens, softmax_scale,
     prefill_block_table / prefill_cu_seqlens_q (from the first prefill row) /
     prefill_seq_lens; a part with no rows needs none of its tensors.
     """
+    _check_workspace(workspace)
     if topk.dim() == 3:
         topk = topk[0]
     nd = int(num_decode_tokens)
@@ -413,6 +434,7 @@ def msa_sparse_attention(q, kv: KVCache, topk, num_decode_tokens, softmax_scale,
         nbytes = max(msa_decode_workspace_size(max(nd, 1), hq, d, topk.shape[1]),
                      msa_prefill_workspace_size(num_tokens - nd, hq, d, topk.shape[1]))
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _ws_args(workspace, dev)
     kvs = kv._struct()
     _call("msa_sparse_attention", _ptr(q), MSA_BF16, num_tokens, hq, ctypes.byref(kvs), _ptr(topk), topk.stride(0),
           topk.shape[1], nd, decode_query_len,
@@ -421,8 +443,7 @@ def msa_sparse_attention(q, kv: KVCache, topk, num_decode_tokens, softmax_scale,
           0 if psl is None else psl.shape[0],
           None if pbt is None else _ptr(pbt), 0 if pbt is None else pbt.stride(0), 0 if pbt is None else pbt.shape[1],
           None if pcu is None else _ptr(pcu), None if psl is None else _ptr(psl),
-          float(softmax_scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-          _stream(dev))
+          float(softmax_scale), _ptr(out), ws_ptr, ws_bytes, _stream(dev))
     return out
 
 

@@ -187,6 +187,28 @@ def test_binding_rejects_host_tensors():
         msa.msa_query_token_positions(t(np.array([0, 3], np.int32)), t(np.array([0], np.int32)), 3)
 
 
+def test_binding_rejects_host_or_strided_workspaces():
+    # the library writes up to workspace_bytes bytes from the workspace
+    # pointer on the GPU: a host tensor or a strided view must not reach it
+    import torch
+    from synth import make_workload, make_kv_cache, make_query
+    wl = make_workload("C4s")
+    cache = make_kv_cache(wl, "cpu")
+    kv = msa.KVCache(wl.kv_dtype, cache["k_pages"], cache["v_pages"], wl.num_kv_heads, wl.head_dim)
+    q = make_query(wl, "cpu")
+    t = lambda x: torch.from_numpy(x)
+    args = (q, kv, t(wl.topk), t(wl.block_table), t(wl.cu_seqlens_q), t(wl.seq_lens), wl.softmax_scale)
+    with pytest.raises(ValueError, match="GPU"):
+        msa.msa_sparse_prefill(*args, workspace=torch.empty(64, dtype=torch.uint8))
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        msa.msa_sparse_prefill(*args, workspace=bytearray(64))
+    with pytest.raises(ValueError, match="GPU"):
+        msa.msa_sparse_decode(q, kv, t(wl.topk), t(wl.block_table), t(wl.seq_lens), wl.softmax_scale,
+                              workspace=torch.empty(64, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU"):
+        msa.msa_sparse_attention(q, kv, t(wl.topk), 0, wl.softmax_scale, workspace=torch.empty(64, dtype=torch.uint8))
+
+
 def test_binding_rejects_pages_that_are_not_dense():
     import torch
     kp = torch.zeros((4, 2, 16, 256), dtype=torch.bfloat16)[..., :128]    # a head_dim slice of wider rows
