@@ -444,9 +444,12 @@ MSA_API msa_status_t msa_sparse_decode_noalloc(const void* q, int32_t q_dtype, i
                      stream);
 }
 
-// One 32-byte row order per 32-row query tile.  A request of n rows has
-// ceil(n / 32) tiles, so total_q rows in any number of requests have at most
-// total_q + ceil(total_q / 32) tiles.
+// A query tile's row order takes a byte per row of the tile (QT = 32, 48 or
+// 64 rows at 8-6, 5 and 4 query heads per kv head).  A request of n rows has
+// ceil(n / QT) tiles, so at QT = 32 total_q rows in any number of requests
+// have at most total_q + ceil(total_q / 32) tiles; the larger tiles fit this
+// size unless most requests hold a single row (the tiles past it keep their
+// natural order).
 MSA_API size_t msa_prefill_workspace_size(int32_t total_q, int32_t num_q_heads, int32_t head_dim, int32_t topk_k) {
   (void)num_q_heads;
   (void)head_dim;
